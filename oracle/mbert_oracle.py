@@ -265,6 +265,49 @@ def split_qkv(qkv, cfg: Config):
     return parts[:, 0], parts[:, 1], parts[:, 2]
 
 
+def qkv_projection(h, Wqkv, pos, theta: float, cfg: Config, apply_rope: bool = True):
+    """qkv = h Wqkv^T with the query and key parts rotated at each row's position
+    ([KGP] §"How Does ModernBERT Make Q, K and V?"; [CAN] §"The two rope tables": q and k
+    only, every head, rotate-half). Returns [T, 3D] in the fused column order."""
+    qkv = np.asarray(h, dtype=np.float64) @ np.asarray(Wqkv, dtype=np.float64).T
+    if not apply_rope:
+        return qkv
+    T = qkv.shape[0]
+    q, k, v = split_qkv(qkv, cfg)
+    q = rope(q.transpose(1, 0, 2), pos, theta).transpose(1, 0, 2)
+    k = rope(k.transpose(1, 0, 2), pos, theta).transpose(1, 0, 2)
+    return np.concatenate([q.reshape(T, -1), k.reshape(T, -1), v.reshape(T, -1)], axis=1)
+
+
+def attention_varlen(qkv, segments, is_global: bool, cfg: Config) -> np.ndarray:
+    """Attention of a packed batch: each segment (start, end, key_valid or None) is one
+    sequence; heads are concatenated back in order ([SBD] §"Implementing it"). Returns
+    [T, D]."""
+    q, k, v = split_qkv(np.asarray(qkv, dtype=np.float64), cfg)
+    a = np.zeros_like(q)
+    for (s0, s1, key_valid) in segments:
+        if s1 > s0:
+            a[s0:s1] = attention_sequence(q[s0:s1], k[s0:s1], v[s0:s1], is_global,
+                                          cfg.half_window, key_valid)
+    return a.reshape(q.shape[0], cfg.hidden)
+
+
+def segments_of(cu_seqlens):
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    return [(int(cu[s]), int(cu[s + 1]), None) for s in range(len(cu) - 1)]
+
+
+def residual_linear(x, a, W) -> np.ndarray:
+    """x + a W^T: a bias-free Linear added back to the residual stream ([KGP] §"What Does
+    LayerNorm Do?": after each block its output is added back to its input)."""
+    return np.asarray(x, dtype=np.float64) + np.asarray(a, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T
+
+
+def mlp_in_geglu(h, Wi, cfg: Config) -> np.ndarray:
+    """geglu(h Wi^T) ([KGP] §"What Does the GeGLU MLP Do?")."""
+    return geglu(np.asarray(h, dtype=np.float64) @ np.asarray(Wi, dtype=np.float64).T, cfg.intermediate)
+
+
 def encoder_layer(x, lw: dict, layer: int, segments, pos, cfg: Config) -> np.ndarray:
     """One pre-norm block ([CAN] §"The pre-norm layer and the final norm";
     [SBD] §"Implementing it"):
@@ -281,21 +324,12 @@ def encoder_layer(x, lw: dict, layer: int, segments, pos, cfg: Config) -> np.nda
         h = x
     else:
         h = layernorm(x, lw["attn_norm"], cfg.eps)
-    q, k, v = split_qkv(h @ np.asarray(lw["Wqkv"], dtype=np.float64).T, cfg)
     theta = cfg.theta_global if g else cfg.theta_local
-    q = rope(q.transpose(1, 0, 2), pos, theta).transpose(1, 0, 2)
-    k = rope(k.transpose(1, 0, 2), pos, theta).transpose(1, 0, 2)
-    a = np.zeros_like(q)
-    for (s0, s1, key_valid) in segments:
-        if s1 > s0:
-            a[s0:s1] = attention_sequence(q[s0:s1], k[s0:s1], v[s0:s1], g, cfg.half_window,
-                                          key_valid)
-    T = x.shape[0]
-    x = x + a.reshape(T, cfg.hidden) @ np.asarray(lw["attn_Wo"], dtype=np.float64).T
+    qkv = qkv_projection(h, lw["Wqkv"], pos, theta, cfg)
+    a = attention_varlen(qkv, segments, g, cfg)
+    x = residual_linear(x, a, lw["attn_Wo"])
     h = layernorm(x, lw["mlp_norm"], cfg.eps)
-    u = h @ np.asarray(lw["Wi"], dtype=np.float64).T
-    x = x + geglu(u, cfg.intermediate) @ np.asarray(lw["mlp_Wo"], dtype=np.float64).T
-    return x
+    return residual_linear(x, mlp_in_geglu(h, lw["Wi"], cfg), lw["mlp_Wo"])
 
 
 def embed(ids, weights: dict, cfg: Config) -> np.ndarray:

@@ -11,3 +11,14 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _library_built():
+    """Tests load the in-tree libmbert.so; build it only when nothing is built yet."""
+    from pathlib import Path
+    lib = Path(ROOT) / "transformer_encoder_amd" / "libmbert.so"
+    if not lib.exists():
+        from transformer_encoder_amd.build import build_library
+        build_library()
+    yield

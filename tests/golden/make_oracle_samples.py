@@ -1,0 +1,70 @@
+"""Writes oracle outputs at sampled rows for the three largest workloads.
+
+The 22-layer float64 oracle needs minutes per 8192-token sequence on a CPU, too long to run
+inside a GPU test, so this script runs it once and stores its outputs at sampled rows (and
+the pooled vectors) in tests/golden/oracle_samples_w{3,4,5}.npz. It calls only oracle/ for the
+values and workloads/ for the seeded inputs. Sequences are independent (attention never
+crosses a cu_seqlens boundary), so running the oracle on one sequence of a packed batch gives
+that sequence's exact outputs.
+
+    python tests/golden/make_oracle_samples.py [3 4 5]
+"""
+from __future__ import annotations
+
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parents[2]
+sys.path.insert(0, str(ROOT))
+
+from oracle import mbert_oracle as O  # noqa: E402
+from workloads import WORKLOADS, make_batch, workload_weights  # noqa: E402
+
+OUT = Path(__file__).resolve().parent
+
+
+def sample_rows(L: int) -> np.ndarray:
+    """Row positions inside one sequence: the edges of the band and of the 128-row work tiles,
+    every 61st row, and the last rows."""
+    picks = {0, 1, 2, 63, 64, 65, 66, 127, 128, 129, 191, 192, 255, 256, 257}
+    picks |= set(range(0, L, 61))
+    picks |= {L - 1, L - 2, L - 65, L - 66, L - 129}
+    return np.array(sorted(p for p in picks if 0 <= p < L), dtype=np.int64)
+
+
+def seqs_to_sample(wid: int, lengths: np.ndarray) -> list[int]:
+    if wid == 3:
+        return [0]
+    if wid == 5:
+        return [0, len(lengths) - 1]
+    order = np.argsort(lengths, kind="stable")
+    return sorted({int(order[0]), int(order[-1]), 0, len(lengths) - 1, int(order[len(order) // 2])})
+
+
+def main(ids_wanted):
+    for wid in ids_wanted:
+        wl = WORKLOADS[wid]
+        w = workload_weights(wid)
+        b = make_batch(wl)
+        cu = b["cu_seqlens"]
+        rows, vals, pooled, seqs = [], [], [], []
+        for s in seqs_to_sample(wid, b["lengths"]):
+            a, e = int(cu[s]), int(cu[s + 1])
+            t0 = time.time()
+            out, pool = O.encode(b["ids"][a:e], [0, e - a], w, O.Config(n_layers=wl.n_layers))
+            r = sample_rows(e - a)
+            rows.append(a + r)
+            vals.append(out[r].astype(np.float32))
+            pooled.append(pool[0].astype(np.float32))
+            seqs.append(s)
+            print(f"workload {wid} seq {s} L={e - a}: {time.time() - t0:.1f}s", flush=True)
+        np.savez_compressed(OUT / f"oracle_samples_w{wid}.npz", workload=wid, seqs=np.array(seqs),
+                            rows=np.concatenate(rows), out=np.concatenate(vals),
+                            pooled=np.stack(pooled), total=int(cu[-1]))
+
+
+if __name__ == "__main__":
+    main([int(a) for a in sys.argv[1:]] or [3, 4, 5])

@@ -1,0 +1,338 @@
+"""Per-step parity: every per-step entry point of the C ABI against the oracle's step on the
+same seeded inputs. Integer outputs bit-exact; float outputs within TOL_STEP of the oracle's
+float64 result (max |err| / max |ref|). Sizes span several 128-row tiles plus a ragged tail."""
+import numpy as np
+import pytest
+
+from gpu_util import (TOL_STEP, dev, dev_i32, expected_tiles, host, meta_for, rel_err,
+                      split_meta, torch)
+from oracle import mbert_oracle as O
+from workloads import (WORKLOADS, cu_from_lengths, draw_lengths, make_batch, pad_batch,
+                       random_matrix, rng)
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["f32", "bf16", "f16"]
+LENGTH_CASES = {
+    "one300": [300],
+    "edges": [1, 64, 65, 129, 130, 0, 7, 256, 127, 128],
+    "one1000": [1000],
+}
+
+
+def B():
+    from transformer_encoder_amd import binding
+    return binding
+
+
+def dt(name):
+    return B().DTYPES[name]
+
+
+def c4_lengths():
+    return draw_lengths(WORKLOADS[4], rng(4, 1))
+
+
+# ---------------------------------------------------------------------------- meta (exact)
+@pytest.mark.parametrize("lengths", [[300], LENGTH_CASES["edges"], [8192], [0], [5, 0, 0, 3],
+                                     "c4"], ids=["300", "edges", "8192", "empty", "zeros", "c4"])
+def test_pack_meta_bit_exact(lengths):
+    if lengths == "c4":
+        lengths = list(c4_lengths())
+    cu = cu_from_lengths(lengths)
+    T, S = int(cu[-1]), len(lengths)
+    m = host(meta_for(cu, T))
+    counts, pos, first, tiles = split_meta(m, T, S)
+    exp_tiles, exp_first = expected_tiles(cu, B().mbert_tile_tokens())
+    assert list(counts[:4]) == [T, max(lengths), len(exp_tiles), 0]
+    assert np.array_equal(pos, O.positions(cu))
+    assert np.array_equal(first, exp_first)
+    assert np.array_equal(tiles, exp_tiles)
+
+
+@pytest.mark.parametrize("cu,total,bit", [([0, 5, 3], 3, 1), ([0, 4, 8], 9, 1), ([1, 4], 4, 1),
+                                          ([0, 8193], 8193, 2)])
+def test_pack_meta_rejects_bad_cu(cu, total, bit):
+    S = len(cu) - 1
+    meta = torch().zeros(B().mbert_meta_ints(total, S), dtype=torch().int32, device="cuda")
+    B().mbert_pack_meta(dev_i32(cu), S, total, 8192, meta)
+    st = B().mbert_read_status(meta)
+    assert st[3] & bit and st[2] == 0
+
+
+def _unpad_gpu(ids_pad, mask, max_pos=8192):
+    Bn, Tp = mask.shape
+    t = torch()
+    Tm = Bn * Tp
+    bufs = {k: t.full((max(Tm, 1),), -5, dtype=t.int32, device="cuda") for k in ("ids", "indices", "rowmap")}
+    cu = t.full((Bn + 1,), -5, dtype=t.int32, device="cuda")
+    meta = t.full((B().mbert_meta_ints(Tm, Bn),), -5, dtype=t.int32, device="cuda")
+    B().mbert_unpad(dev_i32(ids_pad), dev_i32(mask), Bn, Tp, max_pos, bufs["ids"], bufs["indices"],
+                    bufs["rowmap"], cu, meta)
+    return {k: host(v) for k, v in bufs.items()}, host(cu), host(meta)
+
+
+def test_unpad_bit_exact_padded_workload():
+    b = make_batch(WORKLOADS[2])
+    ref = O.unpad(b["ids_pad"], b["mask"])
+    got, cu, meta = _unpad_gpu(b["ids_pad"], b["mask"])
+    Bn, Tp = b["mask"].shape
+    T = len(ref["ids"])
+    counts, pos, first, tiles = split_meta(meta, Bn * Tp, Bn)
+    assert list(counts[:4]) == [T, ref["max_seqlen"], len(expected_tiles(ref["cu_seqlens"], 128)[0]), 0]
+    assert np.array_equal(cu, ref["cu_seqlens"])
+    assert np.array_equal(got["ids"][:T], ref["ids"])
+    assert np.array_equal(got["indices"][:T], ref["indices"])
+    assert np.array_equal(pos[:T], ref["pos"])
+    rowmap = np.full(Bn * Tp, -1)
+    rowmap[ref["indices"]] = np.arange(T)
+    assert np.array_equal(got["rowmap"], rowmap)
+    assert np.array_equal(tiles, expected_tiles(ref["cu_seqlens"], 128)[0])
+
+
+def test_unpad_edges_and_holes():
+    g = np.random.default_rng(5)
+    mask = np.zeros((5, 300), dtype=np.int64)
+    mask[1] = 1                       # full row
+    mask[2, :1] = 1                   # one token
+    mask[3, ::3] = 1                  # holes: positions are ranks among real tokens
+    mask[4, :257] = 1
+    ids_pad = g.integers(0, 50368, size=mask.shape)
+    ref = O.unpad(ids_pad, mask)
+    got, cu, meta = _unpad_gpu(ids_pad, mask)
+    T = len(ref["ids"])
+    counts, pos, _, _ = split_meta(meta, mask.size, 5)
+    assert counts[0] == T and counts[3] == 0
+    assert np.array_equal(cu, ref["cu_seqlens"])
+    assert np.array_equal(got["ids"][:T], ref["ids"]) and np.array_equal(pos[:T], ref["pos"])
+    assert np.array_equal(got["indices"][:T], ref["indices"])
+    mask[0, 3] = 2
+    _, _, meta = _unpad_gpu(ids_pad, mask)
+    assert meta[3] & B().STATUS_BAD_MASK
+
+
+@pytest.mark.parametrize("case", list(LENGTH_CASES) + ["c4"])
+@pytest.mark.parametrize("W", [64, 3, 0])
+def test_key_ranges_bit_exact(case, W):
+    lengths = list(c4_lengths()) if case == "c4" else LENGTH_CASES[case]
+    cu = cu_from_lengths(lengths)
+    T, S = int(cu[-1]), len(lengths)
+    meta = meta_for(cu, T)
+    t = torch()
+    for glob in (True, False):
+        lo = t.full((T,), -9, dtype=t.int32, device="cuda")
+        hi = t.full((T,), -9, dtype=t.int32, device="cuda")
+        B().mbert_attn_key_ranges(meta, T, S, glob, W, lo, hi)
+        rlo, rhi = O.key_ranges(cu, glob, W)
+        assert np.array_equal(host(lo), rlo) and np.array_equal(host(hi), rhi)
+
+
+def test_rope_tables():
+    cfg = B().mbert_default_config()
+    tab = torch().empty(B().mbert_rope_table_floats(cfg), dtype=torch().float32, device="cuda")
+    B().mbert_build_rope_tables(cfg, tab)
+    got = host(tab).reshape(2, 8192, 32, 2)
+    p = np.arange(8192, dtype=np.float64)[:, None]
+    for t, theta in enumerate((160000.0, 10000.0)):
+        ang = p * O.rope_inv_freq(theta, 64)[None, :]
+        assert np.max(np.abs(got[t, :, :, 0] - np.cos(ang))) < 1.2e-7
+        assert np.max(np.abs(got[t, :, :, 1] - np.sin(ang))) < 1.2e-7
+
+
+# ---------------------------------------------------------------------------- row kernels
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_embed_ln(dtype):
+    V, T = 1000, 333
+    from workloads import round_to
+    E = round_to(random_matrix((V, 768), 31) + 0.3, dtype)
+    w = round_to(1 + random_matrix(768, 32) * 0.05, dtype)
+    ids = np.random.default_rng(33).integers(0, V, size=T)
+    ids[:2] = [0, V - 1]
+    t = torch()
+    resid = t.empty((T, 768), dtype=t.float32, device="cuda")
+    h = t.empty((T, 768), dtype=t.float32 if dtype == "f32" else
+                {"bf16": t.bfloat16, "f16": t.float16}[dtype], device="cuda")
+    B().mbert_embed_ln(dt(dtype), dev_i32(ids), T, None, dev(E, dtype), V, dev(w, dtype), 1e-5,
+                       resid, h)
+    ref = O.embed(ids, {"tok_emb": E, "emb_norm": w}, O.Config(vocab=V))
+    assert rel_err(host(resid), ref) < TOL_STEP["f32"]
+    assert rel_err(host(h), ref) < TOL_STEP[dtype]
+
+
+def test_embed_ln_bad_id_flags_status():
+    V, T = 100, 5
+    E = random_matrix((V, 768), 34, dtype="bf16")
+    w = np.ones(768)
+    ids = np.array([1, 2, V, -1, 3])
+    meta = meta_for([0, T], T)
+    t = torch()
+    resid = t.empty((T, 768), dtype=t.float32, device="cuda")
+    h = t.empty((T, 768), dtype=t.bfloat16, device="cuda")
+    B().mbert_embed_ln(dt("bf16"), dev_i32(ids), T, meta, dev(E, "bf16"), V, dev(w, "bf16"), 1e-5,
+                       resid, h)
+    assert B().mbert_read_status(meta)[3] & B().STATUS_BAD_ID
+    ref = O.embed([0], {"tok_emb": E, "emb_norm": w}, O.Config(vocab=V))
+    assert rel_err(host(resid)[2], ref[0]) < 3e-5
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_layernorm(dtype):
+    T = 517
+    from workloads import round_to
+    x = round_to(random_matrix((T, 768), 41) * 3 + 0.7, "f32")
+    w = round_to(1 + np.random.default_rng(42).standard_normal(768) * 0.02, dtype)
+    t = torch()
+    y = t.empty((T, 768), dtype={"f32": t.float32, "bf16": t.bfloat16, "f16": t.float16}[dtype],
+                device="cuda")
+    B().mbert_layernorm(dt(dtype), dev(x, "f32"), T, None, dev(w, dtype), 1e-5, y)
+    assert rel_err(host(y), O.layernorm(x, w, 1e-5)) < TOL_STEP[dtype]
+
+
+# ---------------------------------------------------------------------------- GEMMs
+def _tdt(dtype):
+    t = torch()
+    return {"f32": t.float32, "bf16": t.bfloat16, "f16": t.float16}[dtype]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("lengths", [[120, 180], [8192]], ids=["300", "8192"])
+@pytest.mark.parametrize("table", [0, 1, None], ids=["global", "local", "norope"])
+def test_qkv_projection(dtype, lengths, table):
+    cu = cu_from_lengths(lengths)
+    T = int(cu[-1])
+    h = random_matrix((T, 768), 51, dtype=dtype)
+    W = random_matrix((2304, 768), 52, dtype=dtype, std=0.02)
+    cfg = B().mbert_default_config()
+    rope = torch().empty(B().mbert_rope_table_floats(cfg), dtype=torch().float32, device="cuda")
+    B().mbert_build_rope_tables(cfg, rope)
+    meta = meta_for(cu, T)
+    qkv = torch().empty((T, 2304), dtype=_tdt(dtype), device="cuda")
+    B().mbert_qkv_rope(dt(dtype), dev(h, dtype), T, meta, dev(W, dtype), rope, 8192, table or 0,
+                       table is not None, qkv)
+    theta = 160000.0 if table == 0 else 10000.0
+    ref = O.qkv_projection(h, W, O.positions(cu), theta, O.Config(), apply_rope=table is not None)
+    assert rel_err(host(qkv), ref) < TOL_STEP[dtype]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_rope_standalone(dtype):
+    cu = cu_from_lengths([77, 300, 5])
+    T = int(cu[-1])
+    x = random_matrix((T, 2304), 61, dtype=dtype)
+    cfg = B().mbert_default_config()
+    rope = torch().empty(B().mbert_rope_table_floats(cfg), dtype=torch().float32, device="cuda")
+    B().mbert_build_rope_tables(cfg, rope)
+    qkv = dev(x, dtype)
+    B().mbert_rope(dt(dtype), qkv, T, meta_for(cu, T), rope, 8192, 1, None)
+    got = host(qkv)
+    q, k, v = O.split_qkv(x, O.Config())
+    pos = O.positions(cu)
+    rq = O.rope(q.transpose(1, 0, 2), pos, 10000.0).transpose(1, 0, 2).reshape(T, -1)
+    rk = O.rope(k.transpose(1, 0, 2), pos, 10000.0).transpose(1, 0, 2).reshape(T, -1)
+    assert rel_err(got[:, :768], rq) < TOL_STEP[dtype]
+    assert rel_err(got[:, 768:1536], rk) < TOL_STEP[dtype]
+    assert np.array_equal(got[:, 1536:], x[:, 1536:])
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("K", [768, 1152])
+@pytest.mark.parametrize("T", [300, 22000])
+def test_linear_residual(dtype, K, T):
+    a = random_matrix((T, K), 71, dtype=dtype)
+    W = random_matrix((768, K), 72, dtype=dtype, std=0.02)
+    r0 = random_matrix((T, 768), 73, dtype="f32")
+    resid = dev(r0, "f32")
+    B().mbert_linear_residual(dt(dtype), dev(a, dtype), K, T, None, dev(W, dtype), resid)
+    ref = O.residual_linear(r0, a, W)
+    assert rel_err(host(resid), ref) < 1e-5
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("T", [300, 4133])
+def test_mlp_in_geglu(dtype, T):
+    h = random_matrix((T, 768), 81, dtype=dtype)
+    Wi = random_matrix((2304, 768), 82, dtype=dtype, std=0.05)
+    m = torch().empty((T, 1152), dtype=_tdt(dtype), device="cuda")
+    B().mbert_mlp_in_geglu(dt(dtype), dev(h, dtype), T, None, dev(Wi, dtype), m)
+    assert rel_err(host(m), O.mlp_in_geglu(h, Wi, O.Config())) < TOL_STEP[dtype]
+
+
+def test_geglu_halves_probe():
+    """The first half of Wi's rows feeds GELU, the second half multiplies it (candding,
+    'The feed-forward halves'): with Wi rows j = a e_0 and 1152 + j = b e_0, h = e_0 gives
+    gelu(a) * b, not gelu(b) * a."""
+    T = 4
+    h = np.zeros((T, 768))
+    h[:, 0] = 1.0
+    Wi = np.zeros((2304, 768))
+    Wi[:1152, 0] = 1.0
+    Wi[1152:, 0] = 2.0
+    m = torch().empty((T, 1152), dtype=torch().float32, device="cuda")
+    B().mbert_mlp_in_geglu(dt("f32"), dev(h, "f32"), T, None, dev(Wi, "f32"), m)
+    assert np.allclose(host(m), 2.0 * O.gelu_erf(1.0), rtol=1e-6)
+
+
+# ---------------------------------------------------------------------------- attention
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("case", list(LENGTH_CASES))
+@pytest.mark.parametrize("glob", [True, False], ids=["global", "local"])
+@pytest.mark.parametrize("W", [64, 3])
+def test_attention(dtype, case, glob, W):
+    if glob and W != 64:
+        pytest.skip("the window only matters on local layers")
+    cu = cu_from_lengths(LENGTH_CASES[case])
+    T, S = int(cu[-1]), len(cu) - 1
+    qkv = random_matrix((T, 2304), 91, dtype=dtype, std=1.5)
+    o = torch().full((T, 768), float("nan"), dtype=_tdt(dtype), device="cuda")
+    B().mbert_attention(dt(dtype), dev(qkv, dtype), T, meta_for(cu, T), S, glob, W, o)
+    ref = O.attention_varlen(qkv, O.segments_of(cu), glob, O.Config(half_window=W))
+    got = host(o)
+    assert np.all(np.isfinite(got))
+    assert rel_err(got, ref) < TOL_STEP[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16"])
+def test_attention_long_global(dtype):
+    cu = cu_from_lengths([3000, 2100])
+    T, S = int(cu[-1]), 2
+    qkv = random_matrix((T, 2304), 92, dtype=dtype, std=1.5)
+    for glob in (True, False):
+        o = torch().empty((T, 768), dtype=_tdt(dtype), device="cuda")
+        B().mbert_attention(dt(dtype), dev(qkv, dtype), T, meta_for(cu, T), S, glob, 64, o)
+        ref = O.attention_varlen(qkv, O.segments_of(cu), glob, O.Config())
+        assert rel_err(host(o), ref) < TOL_STEP[dtype]
+
+
+# ---------------------------------------------------------------------------- final LN + pool
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("case", ["edges", "one1000"])
+def test_final_ln_pool(dtype, case):
+    lengths = LENGTH_CASES[case]
+    cu = cu_from_lengths(lengths)
+    T, S = int(cu[-1]), len(lengths)
+    from workloads import round_to
+    x = round_to(random_matrix((T, 768), 101) * 2 + 0.1, "f32")
+    w = round_to(1 + np.random.default_rng(102).standard_normal(768) * 0.02, dtype)
+    t = torch()
+    out = t.empty((T, 768), dtype=t.float32, device="cuda")
+    pooled = t.full((S, 768), float("nan"), dtype=t.float32, device="cuda")
+    part = t.empty(B().mbert_pool_partial_floats(T, S), dtype=t.float32, device="cuda")
+    B().mbert_final_ln_pool(dev(x, "f32"), T, meta_for(cu, T), S, dt(dtype), dev(w, dtype), 1e-5,
+                            out, pooled, part)
+    ref = O.layernorm(x, w, 1e-5)
+    assert rel_err(host(out), ref) < 3e-5
+    rp = O.mean_pool_normalize(ref, cu)
+    assert np.max(np.abs(host(pooled) - rp)) < 2e-5
+
+
+def test_repad():
+    b = make_batch(WORKLOADS[2])
+    ref = O.unpad(b["ids_pad"], b["mask"])
+    got, _, _ = _unpad_gpu(b["ids_pad"], b["mask"])
+    T = len(ref["ids"])
+    Bn, Tp = b["mask"].shape
+    x = random_matrix((T, 768), 111, dtype="f32")
+    t = torch()
+    out_pad = t.full((Bn, Tp, 768), float("nan"), dtype=t.float32, device="cuda")
+    B().mbert_repad(dev(x, "f32"), dev_i32(got["rowmap"]), Bn, Tp, out_pad)
+    assert np.array_equal(host(out_pad), O.repad(x, ref["indices"], Bn, Tp))

@@ -1,0 +1,61 @@
+"""Builds libmbert.so (the C-ABI library) from csrc/ with hipcc for gfx950, in-tree."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+INCLUDE = ROOT / "include"
+BUILD = PKG / "_build"
+LIB = PKG / "libmbert.so"
+
+SOURCES = ["api.hip", "k_meta.hip", "k_norm.hip", "k_gemm.hip", "k_attn.hip"]
+
+# Packed-fp32 VALU ops are disabled for all device code (-packed-fp32-ops).
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wno-unused-command-line-argument", f"-I{INCLUDE}"]
+
+
+def _hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libmbert.so")
+
+
+def _run(cmd: list[str]) -> None:
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    lines = [ln for ln in proc.stdout.splitlines() if "is not a recognized feature" not in ln]
+    if proc.returncode != 0:
+        raise RuntimeError("build step failed: " + " ".join(cmd) + "\n" + "\n".join(lines))
+
+
+def build_library(jobs: int | None = None, verbose: bool = False) -> Path:
+    """Compile every source and link libmbert.so. Always rebuilds."""
+    hipcc = _hipcc()
+    BUILD.mkdir(exist_ok=True)
+    objs = [BUILD / (Path(s).stem + ".o") for s in SOURCES]
+    cmds = [[hipcc, *HIP_FLAGS, "-c", str(CSRC / s), "-o", str(o)] for s, o in zip(SOURCES, objs)]
+    jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        for cmd, fut in zip(cmds, [ex.submit(_run, c) for c in cmds]):
+            fut.result()
+            if verbose:
+                print("compiled", cmd[-3], flush=True)
+    tmp = LIB.with_suffix(".so.tmp")
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    path = build_library(verbose=True)
+    print(path)
+    sys.exit(0)

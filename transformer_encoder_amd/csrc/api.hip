@@ -1,0 +1,595 @@
+// The C ABI (include/mbert.h): argument validation, workspace layout, layer sequencing,
+// HIP graph capture and per-kernel timing. Host code only; every step of the forward runs
+// in the kernels of k_meta / k_norm / k_gemm / k_attn.
+#include <climits>
+#include <new>
+#include <vector>
+
+#include "common.hpp"
+
+using namespace mb;
+
+namespace {
+
+constexpr int kVersion = 100;  // 1.00
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_dtype(mbert_dtype dt) {
+    return (dt == MBERT_F32 || dt == MBERT_BF16 || dt == MBERT_F16) ? MBERT_OK : MBERT_EUNSUPPORTED;
+}
+size_t dsize(mbert_dtype dt) { return dt == MBERT_F32 ? 4 : (dt == MBERT_BF16 || dt == MBERT_F16) ? 2 : 0; }
+
+int check_cfg(const mbert_config* c) {
+    if (!c) return MBERT_EINVAL;
+    if (c->hidden != D || c->n_heads != NH || c->head_dim != HD || c->intermediate != FF)
+        return MBERT_EUNSUPPORTED;
+    if (c->n_layers < 1 || c->n_layers > 4096 || c->vocab < 1 || c->global_every < 1)
+        return MBERT_EINVAL;
+    if (c->half_window < 0 || c->half_window > 65536) return MBERT_EINVAL;
+    if (c->max_positions < 1 || c->max_positions > (1 << 20)) return MBERT_ERANGE;
+    if (!(c->theta_global > 0.0) || !(c->theta_local > 0.0) || !(c->norm_eps >= 0.0f))
+        return MBERT_EINVAL;
+    return MBERT_OK;
+}
+
+// Rows are addressed with 32-bit products of row and 2304 columns in places; keep totals small
+// enough that every element offset fits comfortably in size_t and every count in int.
+constexpr long kMaxRows = (long)INT_MAX / QKV;
+
+int check_sizes(int total, int n_seqs) {
+    if (total < 0 || n_seqs < 0) return MBERT_EINVAL;
+    if (total > kMaxRows) return MBERT_ERANGE;
+    return MBERT_OK;
+}
+
+int check_weights(const mbert_weights* w) {
+    if (!w) return MBERT_EINVAL;
+    int rc = check_cfg(&w->cfg);
+    if (rc) return rc;
+    if ((rc = check_dtype(w->dtype))) return rc;
+    if (!w->tok_emb || !w->emb_norm || !w->final_norm || !w->layers || !w->rope) return MBERT_EINVAL;
+    for (int l = 0; l < w->cfg.n_layers; ++l) {
+        const mbert_layer_weights& L = w->layers[l];
+        if (!L.Wqkv || !L.attn_Wo || !L.mlp_norm || !L.Wi || !L.mlp_Wo) return MBERT_EINVAL;
+        if ((l == 0) != (L.attn_norm == nullptr)) return MBERT_EINVAL;  // identity on layer 0 only
+    }
+    return MBERT_OK;
+}
+
+mbert_ws_layout make_layout(mbert_dtype dt, int total_max, int n_seqs) {
+    mbert_ws_layout L{};
+    const size_t T = (size_t)total_max;
+    const size_t ds = dsize(dt);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    L.resid = take(T * D * 4);
+    L.h = take(T * D * ds);
+    L.qkv = take(T * QKV * ds);
+    L.meta = take(meta_ints(total_max, n_seqs) * 4);
+    L.partials = take(tiles_max_for(total_max, n_seqs) * D * 4);
+    L.ids = take(T * 4);
+    L.indices = take(T * 4);
+    L.rowmap = take(T * 4);
+    L.cu = take(((size_t)n_seqs + 1) * 4);
+    L.out = take(T * D * 4);
+    L.total_bytes = off;
+    return L;
+}
+
+// ---------------------------------------------------------------- per-kernel timing
+struct Recorder {
+    mbert_timer* t = nullptr;
+    int kind = -1;
+};
+
+}  // namespace
+
+struct mbert_timer {
+    std::vector<hipEvent_t> ev;  // 2 per launch
+    int used = 0;                // launches recorded since the last reset
+};
+
+struct mbert_graph {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+inline void rec_begin(Recorder* r, int kind, hipStream_t s) {
+    if (r && r->t && r->kind == kind && 2 * r->t->used + 1 < (int)r->t->ev.size())
+        (void)hipEventRecord(r->t->ev[2 * r->t->used], s);
+}
+inline void rec_end(Recorder* r, int kind, hipStream_t s) {
+    if (r && r->t && r->kind == kind && 2 * r->t->used + 1 < (int)r->t->ev.size()) {
+        (void)hipEventRecord(r->t->ev[2 * r->t->used + 1], s);
+        r->t->used++;
+    }
+}
+
+#define MB_TRY(expr)                  \
+    do {                              \
+        const int _rc = (expr);       \
+        if (_rc != MBERT_OK) return _rc; \
+    } while (0)
+
+#define MB_TIMED(rec, kind, s, expr)  \
+    do {                              \
+        rec_begin(rec, kind, s);      \
+        const int _rc = (expr);       \
+        rec_end(rec, kind, s);        \
+        if (_rc != MBERT_OK) return _rc; \
+    } while (0)
+
+int run_layer(const mbert_weights* w, int layer, int total, int n_seqs, char* ws,
+              const mbert_ws_layout& L, hipStream_t s, Recorder* rec) {
+    const mbert_config& c = w->cfg;
+    const mbert_layer_weights& lw = w->layers[layer];
+    const mbert_dtype dt = w->dtype;
+    const int32_t* meta = reinterpret_cast<const int32_t*>(ws + L.meta);
+    float* resid = reinterpret_cast<float*>(ws + L.resid);
+    void* h = ws + L.h;
+    void* qkv = ws + L.qkv;
+    const bool glob = (layer % c.global_every) == 0;
+    if (layer > 0)
+        MB_TIMED(rec, MBERT_K_LAYERNORM, s,
+                 mbh::launch_layernorm(dt, resid, total, meta, lw.attn_norm, c.norm_eps, h, s));
+    MB_TIMED(rec, MBERT_K_QKV_ROPE, s,
+             mbh::launch_qkv(dt, h, total, meta, lw.Wqkv, w->rope, c.max_positions, glob ? 0 : 1, 1,
+                             qkv, s));
+    MB_TIMED(rec, glob ? MBERT_K_ATTN_GLOBAL : MBERT_K_ATTN_LOCAL, s,
+             mbh::launch_attention(dt, qkv, total, meta, n_seqs, glob ? 1 : 0, c.half_window, h, s));
+    MB_TIMED(rec, MBERT_K_WO_RESID, s,
+             mbh::launch_linear_residual(dt, h, D, total, meta, lw.attn_Wo, resid, s));
+    MB_TIMED(rec, MBERT_K_LAYERNORM, s,
+             mbh::launch_layernorm(dt, resid, total, meta, lw.mlp_norm, c.norm_eps, h, s));
+    MB_TIMED(rec, MBERT_K_WI_GEGLU, s, mbh::launch_geglu(dt, h, total, meta, lw.Wi, qkv, s));
+    MB_TIMED(rec, MBERT_K_WO2_RESID, s,
+             mbh::launch_linear_residual(dt, qkv, FF, total, meta, lw.mlp_Wo, resid, s));
+    return MBERT_OK;
+}
+
+int encode_impl(const mbert_weights* w, const int32_t* ids, const int32_t* cu, int n_seqs,
+                int total, void* ws, size_t ws_bytes, float* out, float* pooled, hipStream_t s,
+                Recorder* rec) {
+    MB_TRY(check_weights(w));
+    MB_TRY(check_sizes(total, n_seqs));
+    if (!ws || !out || !ids || !cu) return MBERT_EINVAL;
+    const mbert_ws_layout L = make_layout(w->dtype, total, n_seqs);
+    if (ws_bytes < L.total_bytes) return MBERT_ENOSPC;
+    char* base = static_cast<char*>(ws);
+    int32_t* meta = reinterpret_cast<int32_t*>(base + L.meta);
+    float* resid = reinterpret_cast<float*>(base + L.resid);
+    MB_TIMED(rec, MBERT_K_META, s,
+             mbh::launch_pack_meta(cu, n_seqs, total, w->cfg.max_positions, meta, s));
+    if (total == 0) {
+        if (pooled && n_seqs > 0)
+            MB_TRY(mbh::launch_final_ln_pool(resid, 0, meta, n_seqs, w->dtype, w->final_norm,
+                                             w->cfg.norm_eps, out, pooled,
+                                             reinterpret_cast<float*>(base + L.partials), s));
+        return MBERT_OK;
+    }
+    MB_TIMED(rec, MBERT_K_EMBED_LN, s,
+             mbh::launch_embed_ln(w->dtype, ids, total, meta, w->tok_emb, w->cfg.vocab,
+                                  w->emb_norm, w->cfg.norm_eps, resid, base + L.h, s));
+    for (int l = 0; l < w->cfg.n_layers; ++l) MB_TRY(run_layer(w, l, total, n_seqs, base, L, s, rec));
+    MB_TIMED(rec, MBERT_K_FINAL_POOL, s,
+             mbh::launch_final_ln_pool(resid, total, meta, n_seqs, w->dtype, w->final_norm,
+                                       w->cfg.norm_eps, out, pooled,
+                                       reinterpret_cast<float*>(base + L.partials), s));
+    return MBERT_OK;
+}
+
+int encode_padded_impl(const mbert_weights* w, const int32_t* ids_pad, const int32_t* mask, int B,
+                       int Tpad, void* ws, size_t ws_bytes, float* out_pad, float* pooled,
+                       hipStream_t s, Recorder* rec) {
+    MB_TRY(check_weights(w));
+    if (B < 0 || Tpad < 0) return MBERT_EINVAL;
+    if ((long)B * (long)Tpad > kMaxRows) return MBERT_ERANGE;
+    if (!ws || !out_pad || !ids_pad || !mask) return MBERT_EINVAL;
+    const int total_max = B * Tpad;
+    const mbert_ws_layout L = make_layout(w->dtype, total_max, B);
+    if (ws_bytes < L.total_bytes) return MBERT_ENOSPC;
+    char* base = static_cast<char*>(ws);
+    int32_t* meta = reinterpret_cast<int32_t*>(base + L.meta);
+    int32_t* ids = reinterpret_cast<int32_t*>(base + L.ids);
+    float* resid = reinterpret_cast<float*>(base + L.resid);
+    float* out = reinterpret_cast<float*>(base + L.out);
+    MB_TIMED(rec, MBERT_K_META, s,
+             mbh::launch_unpad(ids_pad, mask, B, Tpad, w->cfg.max_positions, ids,
+                               reinterpret_cast<int32_t*>(base + L.indices),
+                               reinterpret_cast<int32_t*>(base + L.rowmap),
+                               reinterpret_cast<int32_t*>(base + L.cu), meta, s));
+    if (total_max > 0) {
+        MB_TIMED(rec, MBERT_K_EMBED_LN, s,
+                 mbh::launch_embed_ln(w->dtype, ids, total_max, meta, w->tok_emb, w->cfg.vocab,
+                                      w->emb_norm, w->cfg.norm_eps, resid, base + L.h, s));
+        for (int l = 0; l < w->cfg.n_layers; ++l)
+            MB_TRY(run_layer(w, l, total_max, B, base, L, s, rec));
+    }
+    MB_TIMED(rec, MBERT_K_FINAL_POOL, s,
+             mbh::launch_final_ln_pool(resid, total_max, meta, B, w->dtype, w->final_norm,
+                                       w->cfg.norm_eps, out, pooled,
+                                       reinterpret_cast<float*>(base + L.partials), s));
+    MB_TRY(mbh::launch_repad(out, reinterpret_cast<int32_t*>(base + L.rowmap), B, Tpad, out_pad, s));
+    return MBERT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mbert_version(void) { return kVersion; }
+
+const char* mbert_strerror(int code) {
+    switch (code) {
+        case MBERT_OK: return "ok";
+        case MBERT_EINVAL: return "invalid argument";
+        case MBERT_EUNSUPPORTED: return "unsupported dims or dtype";
+        case MBERT_ERANGE: return "size out of range";
+        case MBERT_ENOSPC: return "workspace too small";
+        case MBERT_EHIP: return "HIP launch or runtime error";
+        default: return "unknown error";
+    }
+}
+
+int mbert_default_config(mbert_config* c) {
+    if (!c) return MBERT_EINVAL;
+    c->n_layers = 22;
+    c->hidden = D;
+    c->n_heads = NH;
+    c->head_dim = HD;
+    c->intermediate = FF;
+    c->vocab = 50368;
+    c->global_every = 3;
+    c->half_window = 64;
+    c->max_positions = 8192;
+    c->theta_global = 160000.0;
+    c->theta_local = 10000.0;
+    c->norm_eps = 1e-5f;
+    return MBERT_OK;
+}
+
+int mbert_check_config(const mbert_config* c) { return check_cfg(c); }
+int mbert_tile_tokens(void) { return TILE; }
+size_t mbert_meta_ints(int total_max, int n_seqs) {
+    if (total_max < 0 || n_seqs < 0) return 0;
+    return meta_ints(total_max, n_seqs);
+}
+size_t mbert_dtype_size(mbert_dtype dt) { return dsize(dt); }
+
+size_t mbert_rope_table_floats(const mbert_config* c) {
+    if (check_cfg(c)) return 0;
+    return (size_t)2 * c->max_positions * (HD / 2) * 2;
+}
+
+int mbert_build_rope_tables(const mbert_config* c, float* table, void* stream) {
+    MB_TRY(check_cfg(c));
+    if (!table) return MBERT_EINVAL;
+    return mbh::launch_rope_tables(table, c->max_positions, c->theta_global, c->theta_local,
+                                   as_stream(stream));
+}
+
+int mbert_pack_meta(const int32_t* cu, int n_seqs, int total, int max_positions, int32_t* meta,
+                    void* stream) {
+    MB_TRY(check_sizes(total, n_seqs));
+    if (!cu || !meta || max_positions < 1) return MBERT_EINVAL;
+    return mbh::launch_pack_meta(cu, n_seqs, total, max_positions, meta, as_stream(stream));
+}
+
+int mbert_unpad(const int32_t* ids_pad, const int32_t* mask, int B, int Tpad, int max_positions,
+                int32_t* ids, int32_t* indices, int32_t* rowmap, int32_t* cu, int32_t* meta,
+                void* stream) {
+    if (B < 0 || Tpad < 0 || max_positions < 1) return MBERT_EINVAL;
+    if ((long)B * Tpad > kMaxRows) return MBERT_ERANGE;
+    if (!cu || !meta) return MBERT_EINVAL;
+    if ((long)B * Tpad > 0 && (!ids_pad || !mask || !ids || !indices || !rowmap)) return MBERT_EINVAL;
+    return mbh::launch_unpad(ids_pad, mask, B, Tpad, max_positions, ids, indices, rowmap, cu, meta,
+                             as_stream(stream));
+}
+
+int mbert_attn_key_ranges(const int32_t* meta, int total_max, int n_seqs, int is_global,
+                          int half_window, int32_t* lo, int32_t* hi, void* stream) {
+    MB_TRY(check_sizes(total_max, n_seqs));
+    if (!meta || !lo || !hi || half_window < 0) return MBERT_EINVAL;
+    return mbh::launch_key_ranges(meta, total_max, n_seqs, is_global ? 1 : 0, half_window, lo, hi,
+                                  as_stream(stream));
+}
+
+int mbert_read_status(const int32_t* meta, int32_t* out4, void* stream) {
+    if (!meta || !out4) return MBERT_EINVAL;
+    const hipStream_t s = as_stream(stream);
+    if (hipMemcpyAsync(out4, meta, 4 * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return MBERT_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return MBERT_EHIP;
+    return MBERT_OK;
+}
+
+int mbert_embed_ln(mbert_dtype dt, const int32_t* ids, int total, const int32_t* meta,
+                   const void* tok_emb, int vocab, const void* norm_w, float eps, float* resid,
+                   void* h, void* stream) {
+    MB_TRY(check_dtype(dt));
+    MB_TRY(check_sizes(total, 0));
+    if (total > 0 && (!ids || !tok_emb || !norm_w || !resid || vocab < 1)) return MBERT_EINVAL;
+    if (dt != MBERT_F32 && total > 0 && !h) return MBERT_EINVAL;
+    return mbh::launch_embed_ln(dt, ids, total, meta, tok_emb, vocab, norm_w, eps, resid, h,
+                                as_stream(stream));
+}
+
+int mbert_layernorm(mbert_dtype dt, const float* x, int total, const int32_t* meta, const void* w,
+                    float eps, void* y, void* stream) {
+    MB_TRY(check_dtype(dt));
+    MB_TRY(check_sizes(total, 0));
+    if (total > 0 && (!x || !w || !y)) return MBERT_EINVAL;
+    return mbh::launch_layernorm(dt, x, total, meta, w, eps, y, as_stream(stream));
+}
+
+int mbert_qkv_rope(mbert_dtype dt, const void* h, int total, const int32_t* meta, const void* Wqkv,
+                   const float* rope, int max_positions, int table, int apply_rope, void* qkv,
+                   void* stream) {
+    MB_TRY(check_dtype(dt));
+    MB_TRY(check_sizes(total, 0));
+    if (total > 0 && (!h || !Wqkv || !qkv)) return MBERT_EINVAL;
+    if (apply_rope && (!meta || !rope || max_positions < 1 || (table != 0 && table != 1)))
+        return MBERT_EINVAL;
+    return mbh::launch_qkv(dt, h, total, meta, Wqkv, rope, max_positions, table, apply_rope, qkv,
+                           as_stream(stream));
+}
+
+int mbert_rope(mbert_dtype dt, void* qkv, int total, const int32_t* meta, const float* rope,
+               int max_positions, int table, void* stream) {
+    MB_TRY(check_dtype(dt));
+    MB_TRY(check_sizes(total, 0));
+    if (!meta || !rope || max_positions < 1 || (table != 0 && table != 1)) return MBERT_EINVAL;
+    if (total > 0 && !qkv) return MBERT_EINVAL;
+    return mbh::launch_rope(dt, qkv, total, meta, rope, max_positions, table, as_stream(stream));
+}
+
+int mbert_attention(mbert_dtype dt, const void* qkv, int total, const int32_t* meta, int n_seqs,
+                    int is_global, int half_window, void* o, void* stream) {
+    MB_TRY(check_dtype(dt));
+    MB_TRY(check_sizes(total, n_seqs));
+    if (!meta || half_window < 0) return MBERT_EINVAL;
+    if (total > 0 && (!qkv || !o)) return MBERT_EINVAL;
+    return mbh::launch_attention(dt, qkv, total, meta, n_seqs, is_global ? 1 : 0, half_window, o,
+                                 as_stream(stream));
+}
+
+int mbert_linear_residual(mbert_dtype dt, const void* a, int K, int total, const int32_t* meta,
+                          const void* W, float* resid, void* stream) {
+    MB_TRY(check_dtype(dt));
+    MB_TRY(check_sizes(total, 0));
+    if (K != D && K != FF) return MBERT_EUNSUPPORTED;
+    if (total > 0 && (!a || !W || !resid)) return MBERT_EINVAL;
+    return mbh::launch_linear_residual(dt, a, K, total, meta, W, resid, as_stream(stream));
+}
+
+int mbert_mlp_in_geglu(mbert_dtype dt, const void* h, int total, const int32_t* meta,
+                       const void* Wi, void* m, void* stream) {
+    MB_TRY(check_dtype(dt));
+    MB_TRY(check_sizes(total, 0));
+    if (total > 0 && (!h || !Wi || !m)) return MBERT_EINVAL;
+    return mbh::launch_geglu(dt, h, total, meta, Wi, m, as_stream(stream));
+}
+
+size_t mbert_pool_partial_floats(int total_max, int n_seqs) {
+    if (total_max < 0 || n_seqs < 0) return 0;
+    return tiles_max_for(total_max, n_seqs) * D;
+}
+
+int mbert_final_ln_pool(const float* resid, int total, const int32_t* meta, int n_seqs,
+                        mbert_dtype dt, const void* w, float eps, float* out, float* pooled,
+                        float* partials, void* stream) {
+    MB_TRY(check_dtype(dt));
+    MB_TRY(check_sizes(total, n_seqs));
+    if (!meta || !w || (total > 0 && (!resid || !out)) || (pooled && !partials)) return MBERT_EINVAL;
+    return mbh::launch_final_ln_pool(resid, total, meta, n_seqs, dt, w, eps, out, pooled, partials,
+                                     as_stream(stream));
+}
+
+int mbert_repad(const float* out, const int32_t* rowmap, int B, int Tpad, float* out_pad,
+                void* stream) {
+    if (B < 0 || Tpad < 0) return MBERT_EINVAL;
+    if ((long)B * Tpad > kMaxRows) return MBERT_ERANGE;
+    if ((long)B * Tpad > 0 && (!out || !rowmap || !out_pad)) return MBERT_EINVAL;
+    return mbh::launch_repad(out, rowmap, B, Tpad, out_pad, as_stream(stream));
+}
+
+size_t mbert_workspace_bytes(const mbert_config* c, mbert_dtype dt, int total_max, int n_seqs) {
+    if (check_cfg(c) || check_dtype(dt) || check_sizes(total_max, n_seqs)) return 0;
+    return make_layout(dt, total_max, n_seqs).total_bytes;
+}
+
+int mbert_workspace_layout(const mbert_config* c, mbert_dtype dt, int total_max, int n_seqs,
+                           mbert_ws_layout* layout) {
+    MB_TRY(check_cfg(c));
+    MB_TRY(check_dtype(dt));
+    MB_TRY(check_sizes(total_max, n_seqs));
+    if (!layout) return MBERT_EINVAL;
+    *layout = make_layout(dt, total_max, n_seqs);
+    return MBERT_OK;
+}
+
+int mbert_layer(const mbert_weights* w, int layer, int total, int n_seqs, void* ws,
+                size_t ws_bytes, void* stream) {
+    MB_TRY(check_weights(w));
+    MB_TRY(check_sizes(total, n_seqs));
+    if (!ws || layer < 0 || layer >= w->cfg.n_layers) return MBERT_EINVAL;
+    const mbert_ws_layout L = make_layout(w->dtype, total, n_seqs);
+    if (ws_bytes < L.total_bytes) return MBERT_ENOSPC;
+    if (total == 0) return MBERT_OK;
+    return run_layer(w, layer, total, n_seqs, static_cast<char*>(ws), L, as_stream(stream), nullptr);
+}
+
+int mbert_encode(const mbert_weights* w, const int32_t* ids, const int32_t* cu, int n_seqs,
+                 int total, void* ws, size_t ws_bytes, float* out, float* pooled, void* stream) {
+    return encode_impl(w, ids, cu, n_seqs, total, ws, ws_bytes, out, pooled, as_stream(stream),
+                       nullptr);
+}
+
+int mbert_encode_padded(const mbert_weights* w, const int32_t* ids_pad, const int32_t* mask, int B,
+                        int Tpad, void* ws, size_t ws_bytes, float* out_pad, float* pooled,
+                        void* stream) {
+    return encode_padded_impl(w, ids_pad, mask, B, Tpad, ws, ws_bytes, out_pad, pooled,
+                              as_stream(stream), nullptr);
+}
+
+// ---------------------------------------------------------------- graphs
+static int capture_common(hipStream_t s, mbert_graph** graph, int (*body)(void*), void* ctx) {
+    if (!graph || s == nullptr) return MBERT_EINVAL;
+    *graph = nullptr;
+    if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess) return MBERT_EHIP;
+    const int rc = body(ctx);
+    hipGraph_t g = nullptr;
+    const hipError_t e = hipStreamEndCapture(s, &g);
+    if (rc != MBERT_OK) {
+        if (g) (void)hipGraphDestroy(g);
+        return rc;
+    }
+    if (e != hipSuccess || !g) return MBERT_EHIP;
+    hipGraphExec_t exec = nullptr;
+    if (hipGraphInstantiate(&exec, g, nullptr, nullptr, 0) != hipSuccess) {
+        (void)hipGraphDestroy(g);
+        return MBERT_EHIP;
+    }
+    mbert_graph* G = new (std::nothrow) mbert_graph;
+    if (!G) {
+        (void)hipGraphExecDestroy(exec);
+        (void)hipGraphDestroy(g);
+        return MBERT_EINVAL;
+    }
+    G->graph = g;
+    G->exec = exec;
+    *graph = G;
+    return MBERT_OK;
+}
+
+struct PackedCtx {
+    const mbert_weights* w;
+    const int32_t *ids, *cu;
+    int n_seqs, total;
+    void* ws;
+    size_t ws_bytes;
+    float *out, *pooled;
+    hipStream_t s;
+};
+struct PaddedCtx {
+    const mbert_weights* w;
+    const int32_t *ids_pad, *mask;
+    int B, Tpad;
+    void* ws;
+    size_t ws_bytes;
+    float *out_pad, *pooled;
+    hipStream_t s;
+};
+
+int mbert_graph_capture(const mbert_weights* w, const int32_t* ids, const int32_t* cu, int n_seqs,
+                        int total, void* ws, size_t ws_bytes, float* out, float* pooled,
+                        void* stream, mbert_graph** graph) {
+    MB_TRY(check_weights(w));  // fail before capture starts
+    PackedCtx c{w, ids, cu, n_seqs, total, ws, ws_bytes, out, pooled, as_stream(stream)};
+    return capture_common(as_stream(stream), graph, [](void* p) {
+        PackedCtx* x = static_cast<PackedCtx*>(p);
+        return encode_impl(x->w, x->ids, x->cu, x->n_seqs, x->total, x->ws, x->ws_bytes, x->out,
+                           x->pooled, x->s, nullptr);
+    }, &c);
+}
+
+int mbert_graph_capture_padded(const mbert_weights* w, const int32_t* ids_pad, const int32_t* mask,
+                               int B, int Tpad, void* ws, size_t ws_bytes, float* out_pad,
+                               float* pooled, void* stream, mbert_graph** graph) {
+    MB_TRY(check_weights(w));
+    PaddedCtx c{w, ids_pad, mask, B, Tpad, ws, ws_bytes, out_pad, pooled, as_stream(stream)};
+    return capture_common(as_stream(stream), graph, [](void* p) {
+        PaddedCtx* x = static_cast<PaddedCtx*>(p);
+        return encode_padded_impl(x->w, x->ids_pad, x->mask, x->B, x->Tpad, x->ws, x->ws_bytes,
+                                  x->out_pad, x->pooled, x->s, nullptr);
+    }, &c);
+}
+
+int mbert_graph_launch(mbert_graph* graph, void* stream) {
+    if (!graph || !graph->exec) return MBERT_EINVAL;
+    return hipGraphLaunch(graph->exec, as_stream(stream)) == hipSuccess ? MBERT_OK : MBERT_EHIP;
+}
+
+int mbert_graph_destroy(mbert_graph* graph) {
+    if (!graph) return MBERT_EINVAL;
+    if (graph->exec) (void)hipGraphExecDestroy(graph->exec);
+    if (graph->graph) (void)hipGraphDestroy(graph->graph);
+    delete graph;
+    return MBERT_OK;
+}
+
+// ---------------------------------------------------------------- timing
+int mbert_timer_create(int max_launches, mbert_timer** timer) {
+    if (!timer || max_launches < 1 || max_launches > (1 << 20)) return MBERT_EINVAL;
+    *timer = nullptr;
+    mbert_timer* t = new (std::nothrow) mbert_timer;
+    if (!t) return MBERT_EINVAL;
+    t->ev.resize(2 * (size_t)max_launches, nullptr);
+    for (auto& e : t->ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            for (auto& f : t->ev)
+                if (f) (void)hipEventDestroy(f);
+            delete t;
+            return MBERT_EHIP;
+        }
+    }
+    *timer = t;
+    return MBERT_OK;
+}
+
+int mbert_timer_reset(mbert_timer* t) {
+    if (!t) return MBERT_EINVAL;
+    t->used = 0;
+    return MBERT_OK;
+}
+
+int mbert_timer_read(mbert_timer* t, int* launches, double* total_ms) {
+    if (!t || !launches || !total_ms) return MBERT_EINVAL;
+    *launches = t->used;
+    *total_ms = 0.0;
+    if (t->used == 0) return MBERT_OK;
+    if (hipEventSynchronize(t->ev[2 * t->used - 1]) != hipSuccess) return MBERT_EHIP;
+    double sum = 0.0;
+    for (int i = 0; i < t->used; ++i) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, t->ev[2 * i], t->ev[2 * i + 1]) != hipSuccess) return MBERT_EHIP;
+        sum += ms;
+    }
+    *total_ms = sum;
+    return MBERT_OK;
+}
+
+int mbert_timer_destroy(mbert_timer* t) {
+    if (!t) return MBERT_EINVAL;
+    for (auto& e : t->ev)
+        if (e) (void)hipEventDestroy(e);
+    delete t;
+    return MBERT_OK;
+}
+
+int mbert_encode_timed(const mbert_weights* w, const int32_t* ids, const int32_t* cu, int n_seqs,
+                       int total, void* ws, size_t ws_bytes, float* out, float* pooled,
+                       void* stream, int kind, mbert_timer* timer) {
+    if (!timer || kind < 0 || kind >= MBERT_K_COUNT) return MBERT_EINVAL;
+    Recorder rec{timer, kind};
+    return encode_impl(w, ids, cu, n_seqs, total, ws, ws_bytes, out, pooled, as_stream(stream), &rec);
+}
+
+int mbert_encode_padded_timed(const mbert_weights* w, const int32_t* ids_pad, const int32_t* mask,
+                              int B, int Tpad, void* ws, size_t ws_bytes, float* out_pad,
+                              float* pooled, void* stream, int kind, mbert_timer* timer) {
+    if (!timer || kind < 0 || kind >= MBERT_K_COUNT) return MBERT_EINVAL;
+    Recorder rec{timer, kind};
+    return encode_padded_impl(w, ids_pad, mask, B, Tpad, ws, ws_bytes, out_pad, pooled,
+                              as_stream(stream), &rec);
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+// Shared device-side definitions for the gfx950 ModernBERT-base encoder kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mbert.h"
+
+namespace mb {
+
+// ModernBERT-base shapes the kernels are specialised to (kgptalkie, "ModernBERT-base
+// Architecture Teardown", §"What Is ModernBERT-base?").
+constexpr int D = 768;        // hidden width
+constexpr int NH = 12;        // heads
+constexpr int HD = 64;        // head width
+constexpr int FF = 1152;      // GeGLU intermediate width
+constexpr int QKV = 3 * D;    // fused projection width
+constexpr int TILE = 128;     // query rows per attention / pooling work tile
+constexpr int NXCD = 8;       // accelerator complex dies on MI355X
+
+typedef __bf16 bf16;
+typedef _Float16 f16;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- element conversion
+template <typename T> __device__ __forceinline__ float to_f(T x) { return static_cast<float>(x); }
+template <typename T> __device__ __forceinline__ T from_f(float x) { return static_cast<T>(x); }
+
+// Four consecutive elements <-> float4 (8-byte loads for 16-bit types, 16-byte for fp32).
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+    typedef float4 raw;
+    __device__ static float4 load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+    __device__ static void store(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+};
+template <> struct Vec4<bf16> {
+    __device__ static float4 load(const bf16* p) {
+        bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+        return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+    }
+    __device__ static void store(bf16* p, float4 v) {
+        bf16x4 o = {(bf16)v.x, (bf16)v.y, (bf16)v.z, (bf16)v.w};
+        *reinterpret_cast<bf16x4*>(p) = o;
+    }
+};
+template <> struct Vec4<f16> {
+    __device__ static float4 load(const f16* p) {
+        f16x4 v = *reinterpret_cast<const f16x4*>(p);
+        return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+    }
+    __device__ static void store(f16* p, float4 v) {
+        f16x4 o = {(f16)v.x, (f16)v.y, (f16)v.z, (f16)v.w};
+        *reinterpret_cast<f16x4*>(p) = o;
+    }
+};
+
+// ---------------------------------------------------------------- wave reductions (wave64)
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// ---------------------------------------------------------------- work distribution
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). Remap the
+// hardware id so that each XCD receives one contiguous range of logical tiles: neighbouring
+// tiles share operands (the same activation rows, the same head's keys), so they hit in the
+// same L2. `n` is the grid size; ids at or beyond n never occur.
+__device__ __forceinline__ int xcd_remap(int hw_id, int n) {
+    const int per = (n + NXCD - 1) / NXCD;
+    const int xcd = hw_id % NXCD;
+    const int local = hw_id / NXCD;
+    return xcd * per + local;  // may be >= n when n % 8 != 0: the caller returns early
+}
+__host__ __device__ inline int xcd_grid(int n) { return ((n + NXCD - 1) / NXCD) * NXCD; }
+
+// ---------------------------------------------------------------- the attention band
+// Keys a query may read, inclusive [lo, hi], as packed token indices: the whole sequence
+// [s0, s1) on a global layer, |i - j| <= W clipped to the sequence on a local layer
+// (candding, "ModernBERT", §"The alternating attention"). Shared by the attention kernel
+// and the key-range debug kernel so the band can be checked exactly.
+__device__ __forceinline__ void key_range(int q, int s0, int s1, int is_global, int W,
+                                          int& lo, int& hi) {
+    if (is_global) {
+        lo = s0;
+        hi = s1 - 1;
+    } else {
+        lo = max(s0, q - W);
+        hi = min(s1 - 1, q + W);
+    }
+}
+
+// Meta buffer offsets (see mbert.h).
+struct MetaView {
+    int* counts;
+    int* seq_tile0;
+    int4* tiles;
+    int* pos;
+};
+__host__ __device__ inline size_t tiles_max_for(int total_max, int n_seqs) {
+    return (size_t)((total_max + TILE - 1) / TILE) + (size_t)n_seqs;
+}
+__host__ __device__ inline MetaView meta_view(int* meta, int total_max, int n_seqs) {
+    MetaView v;
+    v.counts = meta;
+    v.pos = meta + 8;
+    v.seq_tile0 = meta + 8 + total_max;
+    size_t off = 8 + (size_t)total_max + (size_t)n_seqs + 1;
+    off = (off + 3) & ~(size_t)3;  // 16-byte alignment for int4 tiles
+    v.tiles = reinterpret_cast<int4*>(meta + off);
+    return v;
+}
+__host__ __device__ inline size_t meta_ints(int total_max, int n_seqs) {
+    size_t off = 8 + (size_t)total_max + (size_t)n_seqs + 1;
+    off = (off + 3) & ~(size_t)3;
+    return off + 4 * tiles_max_for(total_max, n_seqs);
+}
+
+// Rows to process: the device count when a meta buffer is given, else the host count.
+__device__ __forceinline__ int rows_of(const int* counts, int total) {
+    return counts ? min(total, counts[MBERT_META_TOTAL]) : total;
+}
+
+}  // namespace mb
+
+// Host-side launch helpers (defined in the .hip files; called by api.cpp).
+namespace mbh {
+using mbert_dtype_t = mbert_dtype;
+int launch_rope_tables(float* table, int max_pos, double theta_g, double theta_l, hipStream_t s);
+int launch_pack_meta(const int32_t* cu, int n_seqs, int total, int max_pos, int32_t* meta,
+                     hipStream_t s);
+int launch_unpad(const int32_t* ids_pad, const int32_t* mask, int B, int Tpad, int max_pos,
+                 int32_t* ids, int32_t* indices, int32_t* rowmap, int32_t* cu, int32_t* meta,
+                 hipStream_t s);
+int launch_key_ranges(const int32_t* meta, int total_max, int n_seqs, int is_global, int W,
+                      int32_t* lo, int32_t* hi, hipStream_t s);
+int launch_repad(const float* out, const int32_t* rowmap, int B, int Tpad, float* out_pad,
+                 hipStream_t s);
+int launch_embed_ln(mbert_dtype dt, const int32_t* ids, int total, const int32_t* meta,
+                    const void* emb, int vocab, const void* w, float eps, float* resid, void* h,
+                    hipStream_t s);
+int launch_layernorm(mbert_dtype dt, const float* x, int total, const int32_t* meta,
+                     const void* w, float eps, void* y, hipStream_t s);
+int launch_final_ln_pool(const float* resid, int total, const int32_t* meta, int n_seqs,
+                         mbert_dtype dt, const void* w, float eps, float* out, float* pooled,
+                         float* partials, hipStream_t s);
+int launch_qkv(mbert_dtype dt, const void* h, int total, const int32_t* meta, const void* W,
+               const float* rope, int max_pos, int table, int apply_rope, void* qkv,
+               hipStream_t s);
+int launch_rope(mbert_dtype dt, void* qkv, int total, const int32_t* meta, const float* rope,
+                int max_pos, int table, hipStream_t s);
+int launch_linear_residual(mbert_dtype dt, const void* a, int K, int total, const int32_t* meta,
+                           const void* W, float* resid, hipStream_t s);
+int launch_geglu(mbert_dtype dt, const void* h, int total, const int32_t* meta, const void* Wi,
+                 void* m, hipStream_t s);
+int launch_attention(mbert_dtype dt, const void* qkv, int total, const int32_t* meta, int n_seqs,
+                     int is_global, int W, void* o, hipStream_t s);
+}  // namespace mbh
+
+#define MB_CHECK_LAUNCH()                                   \
+    do {                                                    \
+        if (hipGetLastError() != hipSuccess) return MBERT_EHIP; \
+    } while (0)

@@ -1,0 +1,316 @@
+// Varlen bidirectional attention for one layer: o = softmax(q k^T / 8 + mask) v per head,
+// keys restricted to the query's own sequence, and on local layers to |i - j| <= W
+// (kgptalkie, "ModernBERT-base Architecture Teardown", §"How Does Self-Attention Work?",
+// §"What Are Local and Global Attention?"; candding, "ModernBERT", §"The alternating
+// attention").
+//
+// Work: one workgroup per (work tile of <= 128 query rows of one sequence, head); 4 wave64s,
+// 32 query rows each. K/V tiles of 64 keys stream through two LDS stages (prefetched into
+// registers one tile ahead). The workgroup walks only the keys its band can reach: the whole
+// sequence on a global layer, [q0 - W, q0 + qn - 1 + W] on a local one; a wave whose own
+// band misses a key tile skips its MFMAs for it.
+//
+// Layout trick: each wave computes S^T = K Q^T (32x32 MFMA blocks: rows = keys,
+// columns = queries), so every lane owns one query column: the row max, row sum and the
+// rescaling of the output are per-lane, with one cross-lane exchange (lane ^ 32) for the max.
+// The probabilities then feed O^T = V^T P^T directly as the MFMA B operand (no shuffle);
+// V is stored transposed in LDS ([d][key]) so each lane's 8 keys are two 8-byte reads. The
+// MFMA k-slots of both operands follow the same key permutation (lane group g holds keys
+// 4g..4g+3 and 8+4g..8+4g+3 of each 16-key slice), which leaves the product unchanged.
+// Softmax is online in fp32 with exp2 and the scale 0.125 * log2(e) folded into one multiply.
+// The fp32 variant uses v_mfma_f32_32x32x2_f32 and keeps V in natural layout.
+#include "common.hpp"
+
+namespace mb {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T> struct AttnCfg {
+    static constexpr bool F32 = sizeof(T) == 4;
+    static constexpr int KP = F32 ? 68 : 72;   // K row pitch, elements ([key][d])
+    static constexpr int VP = 68;              // V pitch: fp32 [key][d], 16-bit [d][key]
+    static constexpr int KSZ = 64 * KP;
+    static constexpr int VSZ = 64 * VP;
+};
+
+template <typename T> struct Mma;
+template <> struct Mma<bf16> {
+    __device__ __forceinline__ static void run(const u32x4& a, const u32x4& b, f32x16& c) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static u32x4 pack(const float* p) {
+        bf16x8 v = {(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3],
+                    (bf16)p[4], (bf16)p[5], (bf16)p[6], (bf16)p[7]};
+        return __builtin_bit_cast(u32x4, v);
+    }
+};
+template <> struct Mma<f16> {
+    __device__ __forceinline__ static void run(const u32x4& a, const u32x4& b, f32x16& c) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static u32x4 pack(const float* p) {
+        f16x8 v = {(f16)p[0], (f16)p[1], (f16)p[2], (f16)p[3],
+                   (f16)p[4], (f16)p[5], (f16)p[6], (f16)p[7]};
+        return __builtin_bit_cast(u32x4, v);
+    }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv, T* __restrict__ out,
+                                                      const int* __restrict__ meta, int total_max,
+                                                      int S, int tiles_max, int is_global, int W,
+                                                      float scale_log2) {
+    using C = AttnCfg<T>;
+    constexpr bool F32 = C::F32;
+    __shared__ __align__(16) T Ks[2][C::KSZ];
+    __shared__ __align__(16) T Vs[2][C::VSZ];
+
+    const MetaView mv = meta_view(const_cast<int*>(meta), total_max, S);
+    const int lin = xcd_remap(blockIdx.x, gridDim.x);
+    if (lin >= NH * tiles_max) return;
+    const int head = lin / tiles_max, tile = lin % tiles_max;
+    if (tile >= mv.counts[MBERT_META_NTILES]) return;
+    const int4 tl = mv.tiles[tile];
+    const int q0 = tl.x, qn = tl.y, s0 = tl.z, s1 = tl.w;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, g = lane >> 5;
+    const int qw0 = q0 + 32 * wave;
+    const int qcnt = min(32, qn - 32 * wave);
+
+    int klo, khi, tmp;
+    key_range(q0, s0, s1, is_global, W, klo, tmp);
+    key_range(q0 + qn - 1, s0, s1, is_global, W, tmp, khi);
+    const int nkt = (khi - klo) / 64 + 1;
+
+    // this lane's query (loads clamped into the tile) and its band
+    const int qrow = q0 + min(32 * wave + n, qn - 1);
+    int qlo, qhi;
+    key_range(qw0 + n, s0, s1, is_global, W, qlo, qhi);
+    // keys valid for every query of the wave: [lo of the last query, hi of the first]
+    int wlo = 1, whi = 0, all_lo = 1, all_hi = 0;
+    if (qcnt > 0) {
+        key_range(qw0, s0, s1, is_global, W, wlo, all_hi);
+        key_range(qw0 + qcnt - 1, s0, s1, is_global, W, all_lo, whi);
+    }
+
+    // ---- Q fragment (MFMA B operand: column = query, 16-byte k-chunks)
+    constexpr int NQ = F32 ? 8 : 4;
+    u32x4 qf[NQ];
+    {
+        const T* qp = qkv + (size_t)qrow * QKV + head * HD;
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+            const int d = F32 ? (8 * c + 4 * g) : (16 * c + 8 * g);
+            qf[c] = *(const u32x4*)(qp + d);
+        }
+    }
+
+    // ---- K/V staging
+    constexpr int KCH = F32 ? 4 : 2;  // 16-byte chunks per thread for K (and V for fp32)
+    u32x4 rk[KCH], rv[KCH];
+    auto gload = [&](int it) {
+        const int kb = klo + 64 * it;
+        if constexpr (F32) {
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) {
+                const int key = min(kb + (tid >> 4) + 16 * i, khi);
+                const T* src = qkv + (size_t)key * QKV + head * HD + (tid & 15) * 4;
+                rk[i] = *(const u32x4*)(src + D);
+                rv[i] = *(const u32x4*)(src + 2 * D);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) {
+                const int key = min(kb + (tid >> 3) + 32 * i, khi);
+                rk[i] = *(const u32x4*)(qkv + (size_t)key * QKV + D + head * HD + (tid & 7) * 8);
+            }
+            const int kp = tid >> 3;  // key pair
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int key = min(kb + 2 * kp + i, khi);
+                rv[i] = *(const u32x4*)(qkv + (size_t)key * QKV + 2 * D + head * HD + (tid & 7) * 8);
+            }
+        }
+    };
+    auto sstore = [&](int st) {
+        if constexpr (F32) {
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) {
+                const int off = ((tid >> 4) + 16 * i) * C::KP + (tid & 15) * 4;
+                *(u32x4*)(&Ks[st][off]) = rk[i];
+                *(u32x4*)(&Vs[st][off]) = rv[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < KCH; ++i)
+                *(u32x4*)(&Ks[st][((tid >> 3) + 32 * i) * C::KP + (tid & 7) * 8]) = rk[i];
+            // transpose: Vt[d][key]; one dword holds keys (2kp, 2kp+1) of one d
+            const int kp = tid >> 3, d0 = (tid & 7) * 8;
+            unsigned* vt = reinterpret_cast<unsigned*>(&Vs[st][0]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const unsigned a = rv[0][m], b = rv[1][m];
+                vt[((d0 + 2 * m) * C::VP) / 2 + kp] = (a & 0xFFFFu) | (b << 16);
+                vt[((d0 + 2 * m + 1) * C::VP) / 2 + kp] = (a >> 16) | (b & 0xFFFF0000u);
+            }
+        }
+    };
+
+    f32x16 oacc[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        oacc[0][e] = 0.f;
+        oacc[1][e] = 0.f;
+    }
+    float m_run = -INFINITY, l_run = 0.f;
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int it = 0; it < nkt; ++it) {
+        if (it + 1 < nkt) gload(it + 1);
+        const int kb = klo + 64 * it;
+        const bool active = qcnt > 0 && kb <= whi && kb + 63 >= wlo;
+        if (active) {
+            const int st = it & 1;
+            // ---- S^T = K Q^T for keys kb .. kb+63 (two 32-key blocks)
+            f32x16 sacc[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sacc[kk][e] = 0.f;
+#pragma unroll
+                for (int c = 0; c < NQ; ++c) {
+                    const int d = F32 ? (8 * c + 4 * g) : (16 * c + 8 * g);
+                    const u32x4 a = *(const u32x4*)(&Ks[st][(32 * kk + n) * C::KP + d]);
+                    if constexpr (F32) {
+                        const f32x4 av = __builtin_bit_cast(f32x4, a), bv = __builtin_bit_cast(f32x4, qf[c]);
+#pragma unroll
+                        for (int x = 0; x < 4; ++x)
+                            sacc[kk] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[x], bv[x], sacc[kk], 0, 0, 0);
+                    } else {
+                        Mma<T>::run(a, qf[c], sacc[kk]);
+                    }
+                }
+            }
+            // ---- online softmax (per lane = per query)
+            const bool need_mask = is_global ? (kb + 63 > khi) : !(kb >= all_lo && kb + 63 <= all_hi);
+            float sv[32];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float x = sacc[kk][e] * scale_log2;
+                    if (need_mask) {
+                        const int key = kb + 32 * kk + 8 * (e >> 2) + 4 * g + (e & 3);
+                        if (key < qlo || key > qhi) x = -INFINITY;
+                    }
+                    sv[16 * kk + e] = x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            float lsum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
+                lsum += sv[i];
+            }
+            l_run = l_run * alpha + lsum;
+            m_run = m_new;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                oacc[0][e] *= alpha;
+                oacc[1][e] *= alpha;
+            }
+            // ---- O^T += V^T P^T
+            if constexpr (F32) {
+#pragma unroll
+                for (int db = 0; db < 2; ++db)
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int key = 32 * kk + 8 * (e >> 2) + 4 * g + (e & 3);
+                            const float a = Vs[st][key * C::VP + 32 * db + n];
+                            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, sv[16 * kk + e], oacc[db], 0, 0, 0);
+                        }
+            } else {
+                u32x4 pb[2][2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) pb[kk][h] = Mma<T>::pack(&sv[16 * kk + 8 * h]);
+#pragma unroll
+                for (int db = 0; db < 2; ++db)
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const T* base = &Vs[st][(32 * db + n) * C::VP + 32 * kk + 16 * h + 4 * g];
+                            const u32x2 lo = *(const u32x2*)base;
+                            const u32x2 hi = *(const u32x2*)(base + 8);
+                            const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+                            Mma<T>::run(a, pb[kk][h], oacc[db]);
+                        }
+            }
+        }
+        if (it + 1 < nkt) sstore((it + 1) & 1);
+        __syncthreads();
+    }
+
+    // ---- normalise and write: lane holds d = 32 db + 8 j + 4 g + i of its query
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (n < qcnt) {
+        const float inv = 1.0f / l_tot;
+        T* op = out + (size_t)(qw0 + n) * D + head * HD;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 v = make_float4(oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv,
+                                             oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
+                Vec4<T>::store(op + 32 * db + 8 * j + 4 * g, v);
+            }
+    }
+}
+
+}  // namespace mb
+
+namespace mbh {
+using namespace mb;
+
+int launch_attention(mbert_dtype dt, const void* qkv, int total, const int32_t* meta, int n_seqs,
+                     int is_global, int W, void* o, hipStream_t s) {
+    const int tmax = (int)tiles_max_for(total, n_seqs);
+    if (tmax == 0) return MBERT_OK;
+    const unsigned grid = (unsigned)xcd_grid(NH * tmax);
+    const float scale_log2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
+    switch (dt) {
+        case MBERT_F32:
+            attn_kernel<float><<<grid, 256, 0, s>>>((const float*)qkv, (float*)o, meta, total, n_seqs,
+                                                    tmax, is_global, W, scale_log2);
+            break;
+        case MBERT_BF16:
+            attn_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)qkv, (bf16*)o, meta, total, n_seqs,
+                                                   tmax, is_global, W, scale_log2);
+            break;
+        case MBERT_F16:
+            attn_kernel<f16><<<grid, 256, 0, s>>>((const f16*)qkv, (f16*)o, meta, total, n_seqs,
+                                                  tmax, is_global, W, scale_log2);
+            break;
+        default:
+            return MBERT_EUNSUPPORTED;
+    }
+    MB_CHECK_LAUNCH();
+    return MBERT_OK;
+}
+
+}  // namespace mbh

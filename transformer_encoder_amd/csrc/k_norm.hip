@@ -1,0 +1,279 @@
+// Bandwidth-bound row kernels: embedding gather + LayerNorm, LayerNorm, final LayerNorm with
+// pooling partial sums, pooling, standalone RoPE. One wave64 per 768-wide row: 12 elements
+// per lane, read as three coalesced 4-element chunks, statistics in fp32 by wave reductions.
+#include "common.hpp"
+
+namespace mb {
+
+template <typename T>
+__device__ __forceinline__ void load_row12(const T* row, int lane, float v[12]) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        const float4 x = Vec4<T>::load(row + 4 * (lane + 64 * c));
+        v[4 * c + 0] = x.x;
+        v[4 * c + 1] = x.y;
+        v[4 * c + 2] = x.z;
+        v[4 * c + 3] = x.w;
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_row12(T* row, int lane, const float v[12]) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+        Vec4<T>::store(row + 4 * (lane + 64 * c),
+                       make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]));
+}
+
+// Weight-only LayerNorm of one row held by a wave: mean, biased variance from a second pass,
+// eps inside the square root, times the weight (kgptalkie, "ModernBERT-base Architecture
+// Teardown", §"What Does LayerNorm Do?"; candding, "ModernBERT", §"The pre-norm layer and the
+// final norm").
+template <typename TW>
+__device__ __forceinline__ void layernorm12(float v[12], const TW* w, int lane, float eps) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) s += v[i];
+    const float mean = wave_sum(s) * (1.0f / D);
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+        v[i] -= mean;
+        q += v[i] * v[i];
+    }
+    const float var = wave_sum(q) * (1.0f / D);
+    const float rstd = 1.0f / sqrtf(var + eps);
+    float wv[12];
+    load_row12(w, lane, wv);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) v[i] = v[i] * rstd * wv[i];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void embed_ln_kernel(const int* __restrict__ ids, int total,
+                                                       int* counts, const T* __restrict__ emb,
+                                                       int vocab, const T* __restrict__ w,
+                                                       float eps, float* __restrict__ resid,
+                                                       T* __restrict__ h) {
+    const int lane = threadIdx.x & 63;
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows_of(counts, total)) return;
+    int id = ids[row];
+    if (id < 0 || id >= vocab) {
+        if (lane == 0 && counts) atomicOr(counts + MBERT_META_STATUS, MBERT_STATUS_BAD_ID);
+        id = 0;
+    }
+    float v[12];
+    load_row12(emb + (long)id * D, lane, v);
+    layernorm12(v, w, lane, eps);
+    store_row12(resid + row * D, lane, v);
+    if (h != nullptr && (void*)h != (void*)resid) store_row12(h + row * D, lane, v);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, int total,
+                                                        const int* __restrict__ counts,
+                                                        const T* __restrict__ w, float eps,
+                                                        T* __restrict__ y) {
+    const int lane = threadIdx.x & 63;
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows_of(counts, total)) return;
+    float v[12];
+    load_row12(x + row * D, lane, v);
+    layernorm12(v, w, lane, eps);
+    store_row12(y + row * D, lane, v);
+}
+
+// Final LayerNorm over one work tile (<= 128 rows of one sequence) plus the tile's column sums
+// of the normalised rows, reduced in a fixed order (no atomics: bitwise reproducible).
+template <typename T>
+__global__ __launch_bounds__(256) void final_ln_kernel(const float* __restrict__ resid,
+                                                       const int* __restrict__ meta, int total_max,
+                                                       int S, const T* __restrict__ w, float eps,
+                                                       float* __restrict__ out,
+                                                       float* __restrict__ partials) {
+    __shared__ float red[4][D];
+    const MetaView mv = meta_view(const_cast<int*>(meta), total_max, S);
+    const int b = blockIdx.x;
+    if (b >= mv.counts[MBERT_META_NTILES]) return;
+    const int4 tl = mv.tiles[b];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float acc[12];
+#pragma unroll
+    for (int i = 0; i < 12; ++i) acc[i] = 0.f;
+    for (int r = wave; r < tl.y; r += 4) {
+        const long row = tl.x + r;
+        float v[12];
+        load_row12(resid + row * D, lane, v);
+        layernorm12(v, w, lane, eps);
+        store_row12(out + row * D, lane, v);
+#pragma unroll
+        for (int i = 0; i < 12; ++i) acc[i] += v[i];
+    }
+    if (partials == nullptr) return;
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[wave][4 * (lane + 64 * c) + e] = acc[4 * c + e];
+    __syncthreads();
+    for (int col = threadIdx.x; col < D; col += 256)
+        partials[(long)b * D + col] = ((red[0][col] + red[1][col]) + red[2][col]) + red[3][col];
+}
+
+// Mean over the sequence from the tile partials (in tile order), then L2 normalisation
+// (kgptalkie, §"How Do We Get One Vector per Text?"; safebydesign, "ModernBertModel 22L 768d",
+// §"Implementing it": normalize(pool(x))). An empty sequence pools to zero.
+__global__ __launch_bounds__(256) void pool_kernel(const int* __restrict__ meta, int total_max,
+                                                   int S, const float* __restrict__ partials,
+                                                   float* __restrict__ pooled) {
+    __shared__ float red[4];
+    const MetaView mv = meta_view(const_cast<int*>(meta), total_max, S);
+    const int s = blockIdx.x;
+    const int t0 = mv.seq_tile0[s], t1 = mv.seq_tile0[s + 1];
+    const int L = t1 > t0 ? mv.tiles[t0].w - mv.tiles[t0].z : 0;
+    float m[3];
+    float sq = 0.f;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        const int col = threadIdx.x + 256 * c;
+        float acc = 0.f;
+        for (int b = t0; b < t1; ++b) acc += partials[(long)b * D + col];
+        m[c] = L > 0 ? acc / (float)L : 0.f;
+        sq += m[c] * m[c];
+    }
+    sq = wave_sum(sq);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sq;
+    __syncthreads();
+    const float nrm = sqrtf(((red[0] + red[1]) + red[2]) + red[3]);
+    const float inv = 1.0f / fmaxf(nrm, 1e-12f);
+#pragma unroll
+    for (int c = 0; c < 3; ++c) pooled[(long)s * D + threadIdx.x + 256 * c] = m[c] * inv;
+}
+
+// Standalone rotate-half RoPE on the query and key columns of one qkv row per workgroup
+// (candding, "ModernBERT", §"The two rope tables").
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ qkv, int total,
+                                                   const int* __restrict__ meta,
+                                                   const float2* __restrict__ tab, int max_pos) {
+    const long row = blockIdx.x;
+    if (row >= rows_of(meta, total)) return;
+    const int p = min(max(meta[8 + row], 0), max_pos - 1);  // pos follows the 8 counts
+    T* r = qkv + row * QKV;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        const int j = threadIdx.x + 256 * c;  // 24 heads (q then k) x 32 pairs
+        const int i = j & 31;
+        const int col = (j >> 5) * HD + i;
+        const float2 cs = tab[(long)p * (HD / 2) + i];
+        const float x1 = to_f(r[col]), x2 = to_f(r[col + 32]);
+        r[col] = from_f<T>(x1 * cs.x - x2 * cs.y);
+        r[col + 32] = from_f<T>(x2 * cs.x + x1 * cs.y);
+    }
+}
+
+}  // namespace mb
+
+namespace mbh {
+using namespace mb;
+
+int launch_embed_ln(mbert_dtype dt, const int32_t* ids, int total, const int32_t* meta,
+                    const void* emb, int vocab, const void* w, float eps, float* resid, void* h,
+                    hipStream_t s) {
+    if (total == 0) return MBERT_OK;
+    const unsigned grid = (unsigned)((total + 3) / 4);
+    int* counts = const_cast<int*>(meta);
+    switch (dt) {
+        case MBERT_F32:
+            embed_ln_kernel<float><<<grid, 256, 0, s>>>(ids, total, counts, (const float*)emb, vocab,
+                                                        (const float*)w, eps, resid, (float*)h);
+            break;
+        case MBERT_BF16:
+            embed_ln_kernel<bf16><<<grid, 256, 0, s>>>(ids, total, counts, (const bf16*)emb, vocab,
+                                                       (const bf16*)w, eps, resid, (bf16*)h);
+            break;
+        case MBERT_F16:
+            embed_ln_kernel<f16><<<grid, 256, 0, s>>>(ids, total, counts, (const f16*)emb, vocab,
+                                                      (const f16*)w, eps, resid, (f16*)h);
+            break;
+        default:
+            return MBERT_EUNSUPPORTED;
+    }
+    MB_CHECK_LAUNCH();
+    return MBERT_OK;
+}
+
+int launch_layernorm(mbert_dtype dt, const float* x, int total, const int32_t* meta,
+                     const void* w, float eps, void* y, hipStream_t s) {
+    if (total == 0) return MBERT_OK;
+    const unsigned grid = (unsigned)((total + 3) / 4);
+    switch (dt) {
+        case MBERT_F32:
+            layernorm_kernel<float><<<grid, 256, 0, s>>>(x, total, meta, (const float*)w, eps, (float*)y);
+            break;
+        case MBERT_BF16:
+            layernorm_kernel<bf16><<<grid, 256, 0, s>>>(x, total, meta, (const bf16*)w, eps, (bf16*)y);
+            break;
+        case MBERT_F16:
+            layernorm_kernel<f16><<<grid, 256, 0, s>>>(x, total, meta, (const f16*)w, eps, (f16*)y);
+            break;
+        default:
+            return MBERT_EUNSUPPORTED;
+    }
+    MB_CHECK_LAUNCH();
+    return MBERT_OK;
+}
+
+int launch_final_ln_pool(const float* resid, int total, const int32_t* meta, int n_seqs,
+                         mbert_dtype dt, const void* w, float eps, float* out, float* pooled,
+                         float* partials, hipStream_t s) {
+    const size_t tmax = tiles_max_for(total, n_seqs);
+    if (tmax > 0) {
+        float* part = pooled ? partials : nullptr;
+        switch (dt) {
+            case MBERT_F32:
+                final_ln_kernel<float><<<(unsigned)tmax, 256, 0, s>>>(resid, meta, total, n_seqs,
+                                                                      (const float*)w, eps, out, part);
+                break;
+            case MBERT_BF16:
+                final_ln_kernel<bf16><<<(unsigned)tmax, 256, 0, s>>>(resid, meta, total, n_seqs,
+                                                                     (const bf16*)w, eps, out, part);
+                break;
+            case MBERT_F16:
+                final_ln_kernel<f16><<<(unsigned)tmax, 256, 0, s>>>(resid, meta, total, n_seqs,
+                                                                    (const f16*)w, eps, out, part);
+                break;
+            default:
+                return MBERT_EUNSUPPORTED;
+        }
+        MB_CHECK_LAUNCH();
+    }
+    if (pooled && n_seqs > 0) {
+        pool_kernel<<<n_seqs, 256, 0, s>>>(meta, total, n_seqs, partials, pooled);
+        MB_CHECK_LAUNCH();
+    }
+    return MBERT_OK;
+}
+
+int launch_rope(mbert_dtype dt, void* qkv, int total, const int32_t* meta, const float* rope,
+                int max_pos, int table, hipStream_t s) {
+    if (total == 0) return MBERT_OK;
+    const float2* tab = reinterpret_cast<const float2*>(rope) + (size_t)table * max_pos * (HD / 2);
+    switch (dt) {
+        case MBERT_F32:
+            rope_kernel<float><<<total, 256, 0, s>>>((float*)qkv, total, meta, tab, max_pos);
+            break;
+        case MBERT_BF16:
+            rope_kernel<bf16><<<total, 256, 0, s>>>((bf16*)qkv, total, meta, tab, max_pos);
+            break;
+        case MBERT_F16:
+            rope_kernel<f16><<<total, 256, 0, s>>>((f16*)qkv, total, meta, tab, max_pos);
+            break;
+        default:
+            return MBERT_EUNSUPPORTED;
+    }
+    MB_CHECK_LAUNCH();
+    return MBERT_OK;
+}
+
+}  // namespace mbh
