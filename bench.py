@@ -1,0 +1,286 @@
+"""Throughput of the ModernBERT-base encoder forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+
+A step is one whole forward of the 22-layer encoder over one batch of synthetic input already
+resident in HBM: unpad -> embedding + LN -> 22 layers -> final LN + pooling -> re-pad for the
+padded workload 2 (batch 8, lengths uniform in [128, 512], padded to 512, bf16, random-init
+weights). The timed region replays the forward captured as one HIP graph (the eager rate is
+reported beside it). Prints one JSON line.
+
+Per-kernel roofline: every launch of the dominant kernel (the kind with the largest share of
+one eager forward) is bracketed with HIP events on the stream it runs on, over the eager timed
+steps; achieved = algorithmic flops (or bytes) per launch / mean launch duration.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "encoded tokens/s, 22L ModernBERT-base bf16 fwd; % bf16 MFMA peak"
+PEAK_MFMA_16BIT = 2500.0    # TFLOP/s, dense bf16/fp16 MFMA, MI355X
+PEAK_MFMA_F32 = 157.3       # TFLOP/s
+PEAK_HBM = 8000.0           # GB/s
+D, QKV, FF = 768, 2304, 1152
+GEMM_FLOPS_PER_TOKEN_LAYER = 2 * (D * QKV + D * D + D * 2 * FF + FF * D)  # 10,027,008
+
+
+def attention_pairs(lengths, is_global, W=64):
+    """In-band (query, key) pairs of one layer: sum L^2 globally, the +-W band locally."""
+    tot = 0
+    for L in lengths:
+        L = int(L)
+        if is_global:
+            tot += L * L
+        else:
+            i = np.arange(L)
+            tot += int((np.minimum(L - 1, i + W) - np.maximum(0, i - W) + 1).sum())
+    return tot
+
+
+def kernel_work(kind, T, lengths, dtype_bytes, n_layers=22, n_global=8):
+    """(bound, algorithmic work per launch, unit) for a kernel kind of one forward."""
+    ds = dtype_bytes
+    if kind == "qkv_rope":
+        return "mfma", 2.0 * T * D * QKV, "TFLOP/s"
+    if kind == "wi_geglu":
+        return "mfma", 2.0 * T * D * 2 * FF, "TFLOP/s"
+    if kind == "attn_global":
+        return "mfma", 4.0 * 64 * 12 * attention_pairs(lengths, True), "TFLOP/s"
+    if kind == "attn_local":
+        return "hbm", float(T * (QKV * ds + D * ds)), "GB/s"
+    if kind == "wo_resid":
+        return "hbm", float(T * D * ds + D * D * ds + 2 * T * D * 4), "GB/s"
+    if kind == "wo2_resid":
+        return "hbm", float(T * FF * ds + D * FF * ds + 2 * T * D * 4), "GB/s"
+    if kind == "layernorm":
+        return "hbm", float(T * (D * 4 + D * ds) + D * ds), "GB/s"
+    if kind == "embed_ln":
+        return "hbm", float(T * (4 + D * ds + D * 4 + D * ds) + D * ds), "GB/s"
+    if kind == "final_pool":
+        return "hbm", float(T * D * 8 + D * ds), "GB/s"
+    return "hbm", float(T * 16), "GB/s"
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted((ROOT / "transformer_encoder_amd" / "csrc").glob("*")):
+        h.update(p.name.encode())
+        h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_kind: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were taken
+    on the current kernel sources; else None."""
+    f = ROOT / "profiles" / f"traffic_{kernel_kind}_{workload}.json"
+    if not f.exists():
+        return None
+    d = json.loads(f.read_text())
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, weights, batch, budget_s=12.0):
+    """The oracle as it is, on the host cores: whole sequences of the same workload, in order
+    and in repeated passes, until about `budget_s` seconds of CPU work have been spent."""
+    from oracle import mbert_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    cfg = O.Config(n_layers=wl.n_layers)
+    cu = batch["cu_seqlens"]
+    S = len(cu) - 1
+    done_tok, t_used, seqs = 0, 0.0, 0
+    while t_used < budget_s:
+        s = seqs % S
+        a, b = int(cu[s]), int(cu[s + 1])
+        t0 = time.perf_counter()
+        O.encode(batch["ids"][a:b], [0, b - a], weights, cfg)
+        t_used += time.perf_counter() - t0
+        done_tok += b - a
+        seqs += 1
+    return {"value": round(done_tok / t_used, 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{seqs} sequences ({done_tok} tokens; {seqs / S:.2f} passes over the "
+                      f"{S} sequences) of the same workload through the float64 numpy oracle, "
+                      f"{t_used:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of the graph")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from transformer_encoder_amd import binding as B
+    from transformer_encoder_amd.model import DeviceModel, int32_device
+    from workloads import WORKLOADS, make_batch, workload_weights
+
+    torch.cuda.set_device(0)
+    wl = WORKLOADS[args.workload]
+    weights = workload_weights(wl.id)
+    batch = make_batch(wl)
+    lengths = batch["lengths"]
+    T = int(batch["cu_seqlens"][-1])
+    S = len(lengths)
+    m = DeviceModel(weights, wl.dtype)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.Stream()
+    padded = wl.layout == "padded"
+    with torch.cuda.stream(stream):
+        if padded:
+            ids_pad, mask = int32_device(batch["ids_pad"], dev), int32_device(batch["mask"], dev)
+            Bn, Tp = batch["mask"].shape
+            ws = m.workspace(Bn * Tp, Bn)
+            out = torch.empty((Bn, Tp, D), dtype=torch.float32, device=dev)
+        else:
+            ids, cu = int32_device(batch["ids"], dev), int32_device(batch["cu_seqlens"], dev)
+            ws = m.workspace(T, S)
+            out = torch.empty((T, D), dtype=torch.float32, device=dev)
+        pooled = torch.empty((S, D), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def eager(kind=None, timer=None):
+        if padded:
+            if timer is None:
+                B.mbert_encode_padded(m.w, ids_pad, mask, Bn, Tp, ws, ws.numel(), out, pooled, stream)
+            else:
+                B.mbert_encode_padded_timed(m.w, ids_pad, mask, Bn, Tp, ws, ws.numel(), out, pooled,
+                                            kind, timer, stream)
+        else:
+            if timer is None:
+                B.mbert_encode(m.w, ids, cu, S, T, ws, ws.numel(), out, pooled, stream)
+            else:
+                B.mbert_encode_timed(m.w, ids, cu, S, T, ws, ws.numel(), out, pooled, kind, timer,
+                                     stream)
+
+    max_launches = max(64, 64 * (args.steps + 2))
+    timer = B.mbert_timer_create(max_launches)
+    # ---- which kernel kind dominates one eager forward
+    for _ in range(max(1, args.warmup)):
+        eager()
+    stream.synchronize()
+    share = {}
+    for name, kind in B.KERNEL_KINDS.items():
+        B.mbert_timer_reset(timer)
+        eager(kind, timer)
+        n, ms = B.mbert_timer_read(timer)
+        share[name] = ms
+    dominant = max(share, key=share.get)
+    dom_kind = B.KERNEL_KINDS[dominant]
+
+    # ---- eager timed region (events around every dominant-kernel launch)
+    B.mbert_timer_reset(timer)
+    t0e, t1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream.synchronize()
+    t0e.record(stream)
+    for _ in range(args.steps):
+        eager(dom_kind, timer)
+    t1e.record(stream)
+    stream.synchronize()
+    eager_ms = t0e.elapsed_time(t1e) / args.steps
+    n_launch, dom_ms_total = B.mbert_timer_read(timer)
+    dom_avg_ms = dom_ms_total / max(n_launch, 1)
+
+    # ---- graph-replayed timed region
+    gws = torch.empty_like(ws)
+    gout = torch.empty_like(out)
+    gpool = torch.empty_like(pooled)
+    with torch.cuda.stream(stream):
+        if padded:
+            g = B.mbert_graph_capture_padded(m.w, ids_pad, mask, Bn, Tp, gws, gws.numel(), gout,
+                                             gpool, stream)
+        else:
+            g = B.mbert_graph_capture(m.w, ids, cu, S, T, gws, gws.numel(), gout, gpool, stream)
+    for _ in range(args.warmup):
+        B.mbert_graph_launch(g, stream)
+    stream.synchronize()
+    t0g, t1g = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0g.record(stream)
+    for _ in range(args.steps):
+        B.mbert_graph_launch(g, stream)
+    t1g.record(stream)
+    stream.synchronize()
+    graph_ms = t0g.elapsed_time(t1g) / args.steps
+    same = bool(torch.equal(gout, out) and torch.equal(gpool, pooled))
+    B.mbert_graph_destroy(g)
+    B.mbert_timer_destroy(timer)
+
+    ms = eager_ms if args.eager else graph_ms
+    tokens_per_s = T / (ms * 1e-3)
+    pairs_g = attention_pairs(lengths, True)
+    pairs_l = attention_pairs(lengths, False)
+    n_layers = wl.n_layers
+    n_glob = len([i for i in range(n_layers) if i % 3 == 0])
+    flops = (GEMM_FLOPS_PER_TOKEN_LAYER * T * n_layers
+             + 3072.0 * (pairs_g * n_glob + pairs_l * (n_layers - n_glob)))
+    peak_mfma = PEAK_MFMA_F32 if wl.dtype == "f32" else PEAK_MFMA_16BIT
+    ds = 4 if wl.dtype == "f32" else 2
+    bound, work, unit = kernel_work(dominant, T, lengths, ds)
+    if bound == "mfma":
+        achieved = work / (dom_avg_ms * 1e-3) / 1e12
+        peak = peak_mfma
+    else:
+        achieved = work / (dom_avg_ms * 1e-3) / 1e9
+        peak = PEAK_HBM
+    traffic = traffic_from_profiles(dominant, wl.name)
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded uniform token ids, random-init N(0,0.02) weights)",
+        "config": {"workload": wl.name, "description": wl.description, "real_tokens": T,
+                   "sequences": S, "padded_to": wl.pad_to, "layers": n_layers,
+                   "timed": "eager launches" if args.eager else "HIP graph replay"},
+        "mfma_peak_frac": round(flops / (ms * 1e-3) / 1e12 / peak_mfma, 4),
+        "algorithmic_tflop_per_step": round(flops / 1e12, 4),
+        "eager_ms_per_step": round(eager_ms, 4),
+        "graph_ms_per_step": round(graph_ms, 4),
+        "graph_matches_eager": same,
+        "kernel_ms_share": {k: round(v, 4) for k, v in sorted(share.items(), key=lambda x: -x[1])},
+        "roofline": {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "launches_timed": n_launch,
+                     "avg_launch_ms": round(dom_avg_ms, 5),
+                     "work_per_launch": work},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, weights, batch)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
