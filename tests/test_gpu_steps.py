@@ -195,7 +195,8 @@ def _tdt(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("lengths", [[120, 180], [8192]], ids=["300", "8192"])
+@pytest.mark.parametrize("lengths", [[120, 180], [8192], [8192, 8192, 131]],
+                         ids=["300", "8192", "16515"])
 @pytest.mark.parametrize("table", [0, 1, None], ids=["global", "local", "norope"])
 def test_qkv_projection(dtype, lengths, table):
     cu = cu_from_lengths(lengths)
@@ -236,7 +237,7 @@ def test_rope_standalone(dtype):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("K", [768, 1152])
-@pytest.mark.parametrize("T", [300, 22000])
+@pytest.mark.parametrize("T", [300, 22000, 45001])
 def test_linear_residual(dtype, K, T):
     a = random_matrix((T, K), 71, dtype=dtype)
     W = random_matrix((768, K), 72, dtype=dtype, std=0.02)
@@ -248,7 +249,7 @@ def test_linear_residual(dtype, K, T):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("T", [300, 4133])
+@pytest.mark.parametrize("T", [300, 4133, 16500])
 def test_mlp_in_geglu(dtype, T):
     h = random_matrix((T, 768), 81, dtype=dtype)
     Wi = random_matrix((2304, 768), 82, dtype=dtype, std=0.05)

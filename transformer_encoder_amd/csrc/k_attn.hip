@@ -69,10 +69,16 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
     __shared__ __align__(16) T Vs[2][C::VSZ];
 
     const MetaView mv = meta_view(const_cast<int*>(meta), total_max, S);
-    const int lin = xcd_remap(blockIdx.x, gridDim.x);
-    if (lin >= NH * tiles_max) return;
-    const int head = lin / tiles_max, tile = lin % tiles_max;
-    if (tile >= mv.counts[MBERT_META_NTILES]) return;
+    // (head, tile) pairs of the real tile count, spread over the XCDs in contiguous ranges:
+    // the query tiles of one head (which read the same keys) share an L2
+    const int n_tiles = mv.counts[MBERT_META_NTILES];
+    const int n_act = NH * n_tiles;
+    const int per = (n_act + NXCD - 1) / NXCD;
+    const int local = blockIdx.x / NXCD;
+    if (local >= per) return;
+    const int lin = (blockIdx.x % NXCD) * per + local;
+    if (lin >= n_act) return;
+    const int head = lin / n_tiles, tile = lin % n_tiles;
     const int4 tl = mv.tiles[tile];
     const int q0 = tl.x, qn = tl.y, s0 = tl.z, s1 = tl.w;
 

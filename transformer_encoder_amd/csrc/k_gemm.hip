@@ -1,25 +1,34 @@
 // MFMA GEMM for the encoder's four projections: C[M, N] = A[M, K] . B[N, K]^T, both operands
 // K-contiguous (activations row-major, Linear weights stored [out, in]), fp32 accumulation.
 //
-// Tiling: 256 threads = 4 wave64s in a 2x2 arrangement; each wave owns a (BM/2) x (BN/2)
+// Main loop: 256 threads = 4 wave64s in a 2x2 arrangement; each wave owns a (BM/2) x (BN/2)
 // sub-tile made of 32x32 MFMA blocks (v_mfma_f32_32x32x16_{bf16,f16}; fp32 inputs use
 // v_mfma_f32_32x32x2_f32, four per 16-byte operand). K is consumed 128 bytes at a time
-// (64 16-bit or 32 fp32 elements) through two LDS stages: the next K-tile is fetched into
-// registers while the current one feeds the MFMAs, so each iteration needs one barrier.
-// LDS rows are padded to 144 bytes so the 16-byte operand reads of 8 consecutive lanes hit
-// distinct banks.
+// (64 16-bit or 32 fp32 elements). Global loads run P K-tiles ahead of the MFMAs through
+// register staging (K is only 768 or 1152, so a workgroup's whole life is a dozen K-steps and
+// the load latency has to be covered by loads in flight, not by a long loop), and feed two LDS
+// stages, one barrier per K-step. LDS rows are padded to 144 bytes so the 16-byte operand
+// reads of 8 consecutive lanes hit distinct banks.
 //
-// Epilogues (fused, applied to the fp32 accumulators before anything is rounded):
+// Epilogue: the fp32 accumulator tile is staged through LDS (row pitch BN + 8 floats, which
+// keeps the two half-waves of an MFMA block on disjoint banks) and then processed row-major,
+// so every global access is a coalesced 16-byte vector:
 //   STORE : C (dtype) = acc
-//   ROPE  : query/key head columns rotated rotate-half style at each row's position, then
-//           stored (candding, "ModernBERT", §"The two rope tables"); a wave's two 32-column
-//           blocks are dims i and i+32 of one head, so every pair sits in one lane.
+//   ROPE  : query/key columns rotated rotate-half style at each row's position, then stored
+//           (candding, "ModernBERT", §"The two rope tables"); one position load per row and
+//           contiguous {cos, sin} reads from the float64-built table
 //   RESID : resid (fp32) += acc (kgptalkie, §"What Does LayerNorm Do?": the block output is
 //           added back to its input)
-//   GEGLU : m = gelu_erf(u_gate) * u_mult; the B tile interleaves the GELU-branch rows
-//           [n0, n0+32) and the multiplier rows [1152+n0, 1152+n0+32) per wave so the pair of
-//           a column lands in one lane (candding, §"The feed-forward halves").
+//   GEGLU : m = gelu_erf(u_gate) * u_mult; the B tile takes BN/2 rows from the GELU-branch
+//           half of Wi and the same BN/2 rows of the multiplier half, so the pair of every
+//           output column sits in one tile (candding, §"The feed-forward halves").
+// Work distribution: tiles are spread over the 8 XCDs in contiguous ranges counted from the
+// real row count read on the device (the padded path sizes its grid for B * Tpad rows).
 #include "common.hpp"
+
+#ifndef MB_GEMM_BIG_MIN_TILES
+#define MB_GEMM_BIG_MIN_TILES 512
+#endif
 
 namespace mb {
 
@@ -71,36 +80,62 @@ __device__ __forceinline__ float gelu_erf(float z) {
 template <int EPI, int BN>
 __device__ __forceinline__ int b_row(int bn, int r) {
     if constexpr (EPI == EPI_GEGLU) {
-        const int half = r / (BN / 2);            // which wave column
-        const int within = r % (BN / 2);
-        const int blk = within / 32, i = within % 32;  // blk 0: GELU branch, 1: multiplier
-        return blk * FF + bn * (BN / 2) + half * 32 + i;
+        // first BN/2 rows: GELU branch rows bn*BN/2 + r; next BN/2: the multiplier half
+        return (r < BN / 2) ? bn * (BN / 2) + r : FF + bn * (BN / 2) + (r - BN / 2);
     } else {
         return bn * BN + r;
     }
 }
 
-template <typename T, int BM, int BN, int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs p) {
+template <typename T>
+__device__ __forceinline__ void store8(T* dst, const float* v) {
+    if constexpr (sizeof(T) == 4) {
+        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+        typedef T t8 __attribute__((ext_vector_type(8)));
+        t8 o = {(T)v[0], (T)v[1], (T)v[2], (T)v[3], (T)v[4], (T)v[5], (T)v[6], (T)v[7]};
+        *reinterpret_cast<t8*>(dst) = o;
+    }
+}
+
+__device__ __forceinline__ void load8(const float* src, float* v) {
+    const float4 a = *reinterpret_cast<const float4*>(src);
+    const float4 b = *reinterpret_cast<const float4*>(src + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int P>
+__global__ __launch_bounds__(64 * NWM * NWN, (NWM * NWN == 4) ? 2 : 1) void gemm_kernel(GemmArgs p) {
+    constexpr int NT = 64 * NWM * NWN;                    // threads
     constexpr int ROWB = 128, PITCH = 144;
     constexpr int KT = ROWB / (int)sizeof(T);
-    constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-    constexpr int ACH = BM / 32, BCH = BN / 32;
-    static_assert(EPI != EPI_ROPE || FN == 2, "RoPE epilogue needs 64-column wave tiles");
-    static_assert(EPI != EPI_GEGLU || FN == 2, "GeGLU epilogue needs 64-column wave tiles");
-    __shared__ __align__(16) unsigned char smem[2 * (BM + BN) * PITCH];
+    constexpr int WM = BM / NWM, WN = BN / NWN, FM = WM / 32, FN = WN / 32;
+    constexpr int RSTEP = NT / 8;                         // rows per 16-byte-chunk pass
+    constexpr int ACH = BM / RSTEP, BCH = BN / RSTEP;
+    constexpr int CP = BN + 8;                            // epilogue staging pitch (floats)
+    constexpr int EROWS = NWM * 32;                       // rows staged per epilogue pass
+    constexpr int MAIN_BYTES = 2 * (BM + BN) * PITCH;
+    constexpr int EPI_BYTES = EROWS * CP * 4;
+    constexpr int SMEM = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+    static_assert(EPI != EPI_ROPE || BN % 64 == 0, "RoPE tiles hold whole heads");
+    static_assert(BM % RSTEP == 0 && BN % RSTEP == 0, "tile rows must split over the threads");
+    __shared__ __align__(16) unsigned char smem[SMEM];
 
     const int nbn = p.N / BN;
-    const int nbm = (p.M + BM - 1) / BM;
-    const int tile = xcd_remap(blockIdx.x, gridDim.x);
-    if (tile >= nbn * nbm) return;
-    const int bm = tile / nbn, bn = tile % nbn;
     const int M = rows_of(p.counts, p.M);
+    const int n_act = ((M + BM - 1) / BM) * nbn;
+    const int per = (n_act + NXCD - 1) / NXCD;
+    const int local = blockIdx.x / NXCD;
+    if (local >= per) return;
+    const int tile = (blockIdx.x % NXCD) * per + local;
+    if (tile >= n_act) return;
+    const int bm = tile / nbn, bn = tile % nbn;
     const int m0 = bm * BM;
-    if (m0 >= M) return;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / NWN, wn = wave % NWN;
     const int crow = tid >> 3, cchunk = tid & 7;
     const size_t ld = (size_t)p.K * sizeof(T);
 
@@ -108,32 +143,16 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs p) {
     const unsigned char* b_ptr[BCH];
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
-        const int gr = min(m0 + crow + 32 * i, M - 1);
+        const int gr = min(m0 + crow + RSTEP * i, M - 1);
         a_ptr[i] = (const unsigned char*)p.A + (size_t)gr * ld + cchunk * 16;
     }
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
-        const int gr = b_row<EPI, BN>(bn, crow + 32 * i);
+        const int gr = b_row<EPI, BN>(bn, crow + RSTEP * i);
         b_ptr[i] = (const unsigned char*)p.B + (size_t)gr * ld + cchunk * 16;
     }
 
-    u32x4 ra[ACH], rb[BCH];
-    auto gload = [&](int kt) {
-        const size_t off = (size_t)kt * ROWB;
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) ra[i] = *(const u32x4*)(a_ptr[i] + off);
-#pragma unroll
-        for (int i = 0; i < BCH; ++i) rb[i] = *(const u32x4*)(b_ptr[i] + off);
-    };
-    auto sstore = [&](int st) {
-        unsigned char* base = smem + st * (BM + BN) * PITCH;
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) *(u32x4*)(base + (crow + 32 * i) * PITCH + cchunk * 16) = ra[i];
-#pragma unroll
-        for (int i = 0; i < BCH; ++i)
-            *(u32x4*)(base + (BM + crow + 32 * i) * PITCH + cchunk * 16) = rb[i];
-    };
-
+    u32x4 ra[P][ACH], rb[P][BCH];
     f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -143,96 +162,183 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs p) {
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     const int nk = p.K / KT;
-    gload(0);
-    sstore(0);
-    __syncthreads();
     const int lrow = lane & 31, lk = (lane >> 5) * 16;
-    for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) gload(kt + 1);
-        const unsigned char* As = smem + (kt & 1) * (BM + BN) * PITCH;
-        const unsigned char* Bs = As + BM * PITCH;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            u32x4 af[FM], bf[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *(const u32x4*)(As + (wm * WM + 32 * i + lrow) * PITCH + s * 32 + lk);
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                bf[j] = *(const u32x4*)(Bs + (wn * WN + 32 * j + lrow) * PITCH + s * 32 + lk);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) MfmaOp<T>::run(af[i], bf[j], acc[i][j]);
-        }
-        if (kt + 1 < nk) sstore((kt + 1) & 1);
-        __syncthreads();
-    }
 
-    // ---- epilogue: lane holds column (lane & 31) of each 32x32 block and rows
+#define MB_GLOAD(KT_, U_)                                                                 \
+    do {                                                                                  \
+        const size_t off_ = (size_t)(KT_) * ROWB;                                         \
+        _Pragma("unroll") for (int i = 0; i < ACH; ++i) ra[U_][i] = *(const u32x4*)(a_ptr[i] + off_); \
+        _Pragma("unroll") for (int i = 0; i < BCH; ++i) rb[U_][i] = *(const u32x4*)(b_ptr[i] + off_); \
+    } while (0)
+#define MB_SSTORE(U_, ST_)                                                                \
+    do {                                                                                  \
+        unsigned char* base_ = smem + (ST_) * (BM + BN) * PITCH;                          \
+        _Pragma("unroll") for (int i = 0; i < ACH; ++i)                                   \
+            *(u32x4*)(base_ + (crow + RSTEP * i) * PITCH + cchunk * 16) = ra[U_][i];      \
+        _Pragma("unroll") for (int i = 0; i < BCH; ++i)                                   \
+            *(u32x4*)(base_ + (BM + crow + RSTEP * i) * PITCH + cchunk * 16) = rb[U_][i]; \
+    } while (0)
+
+    // Every load is unconditional (the tail re-reads the last K-tile, whose data is never
+    // used): a load issued under a branch leaves the wait-count pass unsure how many loads are
+    // in flight, and it then waits for all of them, prefetch included. nk % P == 0 (checked
+    // on the host), so the unrolled loop needs no guards either.
+#pragma unroll
+    for (int u = 0; u < P; ++u) MB_GLOAD(min(u, nk - 1), u);
+    MB_SSTORE(0, 0);
+    __syncthreads();
+    for (int kt0 = 0; kt0 < nk; kt0 += P) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) {
+            const int kt = kt0 + u;
+            MB_GLOAD(min(kt + P, nk - 1), u);
+            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch at the head of the K-step
+            const unsigned char* As = smem + (kt & 1) * (BM + BN) * PITCH;
+            const unsigned char* Bs = As + BM * PITCH;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                u32x4 af[FM], bf[FN];
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    af[i] = *(const u32x4*)(As + (wm * WM + 32 * i + lrow) * PITCH + s * 32 + lk);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    bf[j] = *(const u32x4*)(Bs + (wn * WN + 32 * j + lrow) * PITCH + s * 32 + lk);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) MfmaOp<T>::run(af[i], bf[j], acc[i][j]);
+            }
+            MB_SSTORE((u + 1) % P, (kt + 1) & 1);
+            __syncthreads();
+        }
+    }
+#undef MB_GLOAD
+#undef MB_SSTORE
+
+    // ---- epilogue, in FM passes: pass i stages block-row i of every wave (EROWS tile rows)
+    //      through LDS. A lane holds column (lane & 31) of each 32x32 block and rows
     //      8 * (e / 4) + 4 * (lane / 32) + (e % 4) for accumulator element e.
+    float* Cs = reinterpret_cast<float*>(smem);
     const int rq = (lane >> 5) * 4;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int row = m0 + wm * WM + 32 * i + 8 * (e >> 2) + rq + (e & 3);
-            if (row >= M) continue;
-            if constexpr (EPI == EPI_STORE) {
-                T* C = (T*)p.C;
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    C[(size_t)row * p.N + bn * BN + wn * WN + 32 * j + lrow] = from_f<T>(acc[i][j][e]);
-            } else if constexpr (EPI == EPI_RESID) {
-                float* R = (float*)p.C;
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    float* r = R + (size_t)row * D + bn * BN + wn * WN + 32 * j + lrow;
-                    *r += acc[i][j][e];
-                }
-            } else if constexpr (EPI == EPI_ROPE) {
-                T* C = (T*)p.C;
-                const int c0 = bn * BN + wn * WN;  // first column of this wave's head
-                float y1 = acc[i][0][e], y2 = acc[i][1][e];
-                if (c0 < 2 * D) {
+            for (int e = 0; e < 16; ++e)
+                Cs[(wm * 32 + 8 * (e >> 2) + rq + (e & 3)) * CP + wn * WN + 32 * j + lrow] = acc[i][j][e];
+        __syncthreads();
+        // staged row sr holds tile row (sr / 32) * WM + 32 * i + sr % 32
+        auto tile_row = [&](int sr) { return m0 + (sr >> 5) * WM + 32 * i + (sr & 31); };
+        if constexpr (EPI == EPI_STORE) {
+            constexpr int CH = BN / 8;
+            T* C = (T*)p.C;
+            for (int idx = tid; idx < EROWS * CH; idx += NT) {
+                const int sr = idx / CH, c = idx % CH, row = tile_row(sr);
+                if (row >= M) continue;
+                float v[8];
+                load8(Cs + sr * CP + 8 * c, v);
+                store8<T>(C + (size_t)row * p.N + bn * BN + 8 * c, v);
+            }
+        } else if constexpr (EPI == EPI_ROPE) {
+            constexpr int NHT = BN / HD;  // heads per tile
+            T* C = (T*)p.C;
+            const int c0 = bn * BN;
+            const bool rot = c0 < 2 * D;  // query and key columns; value columns pass through
+            for (int idx = tid; idx < EROWS * NHT * 4; idx += NT) {
+                const int pc = idx & 3, hh = (idx >> 2) % NHT, sr = idx / (4 * NHT), row = tile_row(sr);
+                if (row >= M) continue;
+                float x1[8], x2[8];
+                const float* x = Cs + sr * CP + HD * hh + 8 * pc;
+                load8(x, x1);
+                load8(x + 32, x2);
+                if (rot) {
                     const int pp = min(max(p.pos[row], 0), p.max_pos - 1);
-                    const float2 cs = p.rope[(size_t)pp * (HD / 2) + lrow];
-                    const float x1 = y1, x2 = y2;
-                    y1 = x1 * cs.x - x2 * cs.y;
-                    y2 = x2 * cs.x + x1 * cs.y;
+                    const float4* cs = reinterpret_cast<const float4*>(p.rope + (size_t)pp * (HD / 2) + 8 * pc);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 t = cs[q];  // {cos, sin} of pairs 2q and 2q+1
+                        const float a0 = x1[2 * q], b0 = x2[2 * q], a1 = x1[2 * q + 1], b1 = x2[2 * q + 1];
+                        x1[2 * q] = a0 * t.x - b0 * t.y;
+                        x2[2 * q] = b0 * t.x + a0 * t.y;
+                        x1[2 * q + 1] = a1 * t.z - b1 * t.w;
+                        x2[2 * q + 1] = b1 * t.z + a1 * t.w;
+                    }
                 }
-                C[(size_t)row * QKV + c0 + lrow] = from_f<T>(y1);
-                C[(size_t)row * QKV + c0 + 32 + lrow] = from_f<T>(y2);
-            } else {  // EPI_GEGLU
-                T* C = (T*)p.C;
-                const int col = bn * (BN / 2) + wn * 32 + lrow;
-                C[(size_t)row * FF + col] = from_f<T>(gelu_erf(acc[i][0][e]) * acc[i][1][e]);
+                T* dst = C + (size_t)row * QKV + c0 + HD * hh + 8 * pc;
+                store8<T>(dst, x1);
+                store8<T>(dst + 32, x2);
+            }
+        } else if constexpr (EPI == EPI_RESID) {
+            constexpr int CH = BN / 4;
+            float* R = (float*)p.C;
+            for (int idx = tid; idx < EROWS * CH; idx += NT) {
+                const int sr = idx / CH, c = idx % CH, row = tile_row(sr);
+                if (row >= M) continue;
+                const float4 a = *reinterpret_cast<const float4*>(Cs + sr * CP + 4 * c);
+                float4* dst = reinterpret_cast<float4*>(R + (size_t)row * D + bn * BN + 4 * c);
+                float4 v = *dst;
+                v.x += a.x;
+                v.y += a.y;
+                v.z += a.z;
+                v.w += a.w;
+                *dst = v;
+            }
+        } else {  // EPI_GEGLU
+            constexpr int HALF = BN / 2, CH = HALF / 8;
+            T* C = (T*)p.C;
+            for (int idx = tid; idx < EROWS * CH; idx += NT) {
+                const int sr = idx / CH, c = idx % CH, row = tile_row(sr);
+                if (row >= M) continue;
+                float g[8], u[8];
+                load8(Cs + sr * CP + 8 * c, g);
+                load8(Cs + sr * CP + HALF + 8 * c, u);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) g[k] = gelu_erf(g[k]) * u[k];
+                store8<T>(C + (size_t)row * FF + bn * HALF + 8 * c, g);
             }
         }
+        __syncthreads();
     }
 }
 
-template <typename T, int BM, int BN, int EPI>
+#ifndef MB_GEMM_PREFETCH
+#define MB_GEMM_PREFETCH 2
+#endif
+constexpr int kPrefetch = MB_GEMM_PREFETCH;
+
+// Tile shapes: "small" 128x128 with 4 waves of 64x64 (2 workgroups per CU) keeps enough
+// workgroups in flight when there are few rows; "large" 256x256 with 8 waves of 128x64 does
+// twice the MFMA work per wave per K-step (and half the LDS bytes per MFMA) once the grid is
+// big enough to fill every CU several times.
+template <typename T, int EPI>
 int run_gemm(const GemmArgs& a, hipStream_t s) {
-    const int nbm = (a.M + BM - 1) / BM, nbn = a.N / BN;
-    const int n = nbm * nbn;
-    if (n == 0) return MBERT_OK;
-    gemm_kernel<T, BM, BN, EPI><<<xcd_grid(n), 256, 0, s>>>(a);
+    if ((a.K * (int)sizeof(T)) % (128 * kPrefetch) != 0) return MBERT_EUNSUPPORTED;
+    const int big = ((a.M + 255) / 256) * (a.N / 256);
+    if (a.N % 256 == 0 && big >= MB_GEMM_BIG_MIN_TILES) {
+        gemm_kernel<T, 256, 256, 2, 4, EPI, kPrefetch><<<xcd_grid(big), 512, 0, s>>>(a);
+    } else {
+        constexpr int BM = (EPI == EPI_RESID) ? 64 : 128;
+        const int n = ((a.M + BM - 1) / BM) * (a.N / 128);
+        if (n == 0) return MBERT_OK;
+        if (EPI == EPI_RESID && ((a.M + 127) / 128) * (a.N / 128) >= 1024)
+            gemm_kernel<T, 128, 128, 2, 2, EPI, kPrefetch><<<xcd_grid(((a.M + 127) / 128) * (a.N / 128)), 256, 0, s>>>(a);
+        else
+            gemm_kernel<T, BM, 128, 2, 2, EPI, kPrefetch><<<xcd_grid(n), 256, 0, s>>>(a);
+    }
     MB_CHECK_LAUNCH();
     return MBERT_OK;
 }
 
 template <typename T>
 int qkv_t(const GemmArgs& a, int apply_rope, hipStream_t s) {
-    return apply_rope ? run_gemm<T, 128, 128, EPI_ROPE>(a, s) : run_gemm<T, 128, 128, EPI_STORE>(a, s);
+    return apply_rope ? run_gemm<T, EPI_ROPE>(a, s) : run_gemm<T, EPI_STORE>(a, s);
 }
 
 template <typename T>
 int resid_t(const GemmArgs& a, hipStream_t s) {
-    // N = 768 gives only 6 column tiles: use 64-row tiles until there are enough row tiles
-    // to fill 256 CUs twice over with 128-row ones.
-    if ((a.M + 127) / 128 * 6 >= 1024) return run_gemm<T, 128, 128, EPI_RESID>(a, s);
-    return run_gemm<T, 64, 128, EPI_RESID>(a, s);
+    return run_gemm<T, EPI_RESID>(a, s);
 }
 
 }  // namespace mb
@@ -291,9 +397,9 @@ int launch_geglu(mbert_dtype dt, const void* h, int total, const int32_t* meta, 
     a.N = 2 * FF;
     a.C = m;
     switch (dt) {
-        case MBERT_F32: return run_gemm<float, 128, 128, EPI_GEGLU>(a, s);
-        case MBERT_BF16: return run_gemm<bf16, 128, 128, EPI_GEGLU>(a, s);
-        case MBERT_F16: return run_gemm<f16, 128, 128, EPI_GEGLU>(a, s);
+        case MBERT_F32: return run_gemm<float, EPI_GEGLU>(a, s);
+        case MBERT_BF16: return run_gemm<bf16, EPI_GEGLU>(a, s);
+        case MBERT_F16: return run_gemm<f16, EPI_GEGLU>(a, s);
         default: return MBERT_EUNSUPPORTED;
     }
 }
