@@ -31,6 +31,8 @@ METRIC = "encoded tokens/s, 22L ModernBERT-base bf16 fwd; % bf16 MFMA peak"
 PEAK_MFMA_16BIT = 2500.0    # TFLOP/s, dense bf16/fp16 MFMA, MI355X
 PEAK_MFMA_F32 = 157.3       # TFLOP/s
 PEAK_HBM = 8000.0           # GB/s
+CALIB_BYTES = 256 << 20     # streaming calibration kernel: reads and writes this many bytes
+CALIB_NAME = "neg_kernel"
 D, QKV, FF = 768, 2304, 1152
 GEMM_FLOPS_PER_TOKEN_LAYER = 2 * (D * QKV + D * D + D * 2 * FF + FF * D)  # 10,027,008
 
@@ -92,6 +94,74 @@ def traffic_from_profiles(kernel_kind: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+GEMM_EPI = {"qkv_rope": 1, "wo_resid": 2, "wo2_resid": 2, "wi_geglu": 3}
+ROW_KERNELS = {"layernorm": "layernorm_kernel", "embed_ln": "embed_ln_kernel",
+               "final_pool": "final_ln_kernel"}
+
+
+def kernel_matches(kind: str, name: str) -> bool:
+    """Whether a kernel symbol from a trace belongs to a kernel kind of the forward."""
+    import re
+    if kind in GEMM_EPI:
+        if "gemm_kernel" not in name:
+            return False
+        ints = [int(x) for x in re.findall(r"Li(\d+)E", name)]
+        return len(ints) >= 5 and ints[4] == GEMM_EPI[kind]
+    if kind in ROW_KERNELS:
+        return ROW_KERNELS[kind] in name
+    return False
+
+
+def traffic_summary(fetch_dir: str, write_dir: str, kind: str, workload: str, commands: list):
+    """HBM bytes per launch of `kind` from two rocprofv3 --pmc runs (FETCH_SIZE and
+    WRITE_SIZE, KiB per dispatch), each scaled by the factor that makes the same counter read
+    CALIB_BYTES for the streaming calibration kernel of the same run."""
+    import csv
+    import glob
+    if kind in ("wo_resid", "wo2_resid"):
+        raise SystemExit("the two residual GEMMs share one kernel symbol; no per-kind counters")
+
+    def per_dispatch(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not f:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        k_vals, c_vals = [], []
+        for r in csv.DictReader(open(f[0])):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if kernel_matches(kind, r["Kernel_Name"]):
+                k_vals.append(v)
+            elif CALIB_NAME in r["Kernel_Name"]:
+                c_vals.append(v)
+        if not k_vals or not c_vals:
+            raise SystemExit(f"{counter}: kernel or calibration dispatches missing in {d}")
+        return sum(k_vals) / len(k_vals), sum(c_vals) / len(c_vals), len(k_vals)
+
+    fk, fc, n_f = per_dispatch(fetch_dir, "FETCH_SIZE")
+    wk, wc, n_w = per_dispatch(write_dir, "WRITE_SIZE")
+    f_scale = (CALIB_BYTES / 1024.0) / fc
+    w_scale = (CALIB_BYTES / 1024.0) / wc
+    total = (fk * f_scale + wk * w_scale) * 1024.0
+    out = {"kernel_kind": kind, "workload": workload, "source_hash": source_hash(),
+           "fetch_kib_per_launch_raw": fk, "write_kib_per_launch_raw": wk,
+           "calib_fetch_kib_raw": fc, "calib_write_kib_raw": wc,
+           "fetch_scale": f_scale, "write_scale": w_scale, "dispatches": [n_f, n_w],
+           "hbm_bytes_per_launch": total, "commands": commands}
+    base = ROOT / "profiles" / f"traffic_{kind}_{workload}"
+    base.with_suffix(".json").write_text(json.dumps(out, indent=1) + "\n")
+    md = [f"# HBM traffic per launch: {kind}, workload {workload}", "",
+          "Counter runs (from the repository root on one MI355X):", "", "```", *commands, "```",
+          "", f"- FETCH_SIZE per {kind} launch: {fk:.1f} KiB (raw), calibration kernel "
+          f"({CALIB_BYTES >> 20} MiB read + written): {fc:.1f} KiB -> scale {f_scale:.4f}",
+          f"- WRITE_SIZE per launch: {wk:.1f} KiB (raw), calibration: {wc:.1f} KiB -> scale "
+          f"{w_scale:.4f}",
+          f"- HBM bytes per launch (scaled): {total / 1e6:.3f} MB over {n_f} / {n_w} dispatches",
+          f"- kernel sources hash: {out['source_hash']}"]
+    base.with_suffix(".md").write_text("\n".join(md) + "\n")
+    print(json.dumps(out))
+
+
 def cpu_baseline(wl, weights, batch, budget_s=12.0):
     """The oracle as it is, on the host cores: whole sequences of the same workload, in order
     and in repeated passes, until about `budget_s` seconds of CPU work have been spent."""
@@ -129,7 +199,18 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of the graph")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_<kind>_<workload>.{json,md} from two "
+                         "rocprofv3 --pmc runs of this script and exit")
+    ap.add_argument("--kind", default="wi_geglu", help="kernel kind for --traffic-summary")
+    ap.add_argument("--command", action="append", default=[],
+                    help="the counter-run commands, recorded in the summary")
     args = ap.parse_args()
+    if args.traffic_summary:
+        from workloads import WORKLOADS
+        traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.kind,
+                        WORKLOADS[args.workload].name, args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
@@ -230,6 +311,14 @@ def main():
     same = bool(torch.equal(gout, out) and torch.equal(gpool, pooled))
     B.mbert_graph_destroy(g)
     B.mbert_timer_destroy(timer)
+
+    # a plain streaming kernel of known size (reads and writes CALIB_BYTES), outside the timed
+    # region: rocprofv3 counter runs scale FETCH_SIZE / WRITE_SIZE by what they read for it
+    calib_src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    torch.neg(calib_src, out=calib_dst)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
 
     ms = eager_ms if args.eager else graph_ms
     tokens_per_s = T / (ms * 1e-3)

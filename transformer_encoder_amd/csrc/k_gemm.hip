@@ -29,6 +29,9 @@
 #ifndef MB_GEMM_BIG_MIN_TILES
 #define MB_GEMM_BIG_MIN_TILES 512
 #endif
+#ifndef MB_GEMM_SMALL_MAX_TILES
+#define MB_GEMM_SMALL_MAX_TILES 1024
+#endif
 
 namespace mb {
 
@@ -106,8 +109,8 @@ __device__ __forceinline__ void load8(const float* src, float* v) {
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int P>
-__global__ __launch_bounds__(64 * NWM * NWN, (NWM * NWN == 4) ? 2 : 1) void gemm_kernel(GemmArgs p) {
+template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int P, int OCC>
+__global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     constexpr int NT = 64 * NWM * NWN;                    // threads
     constexpr int ROWB = 128, PITCH = 144;
     constexpr int KT = ROWB / (int)sizeof(T);
@@ -303,32 +306,36 @@ __global__ __launch_bounds__(64 * NWM * NWN, (NWM * NWN == 4) ? 2 : 1) void gemm
     }
 }
 
+
 #ifndef MB_GEMM_PREFETCH
 #define MB_GEMM_PREFETCH 2
 #endif
 constexpr int kPrefetch = MB_GEMM_PREFETCH;
 
-// Tile shapes: "small" 128x128 with 4 waves of 64x64 (2 workgroups per CU) keeps enough
-// workgroups in flight when there are few rows; "large" 256x256 with 8 waves of 128x64 does
-// twice the MFMA work per wave per K-step (and half the LDS bytes per MFMA) once the grid is
-// big enough to fill every CU several times.
+// Tile shapes, by grid size (K is 768 or 1152, so a tile lives for only 12-36 K-steps and a
+// small grid is bound by per-workgroup latency and by how evenly the tiles cover 256 CUs):
+//   256x256, 8 waves of 128x64  - many rows: twice the MFMA work per wave per K-step
+//   128x128, 4 waves of 64x64   - the default
+//   128x64 / 64x64, 4 waves     - few rows: more, shorter workgroups spread over more CUs
+template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int OCC>
+int launch_tiles(const GemmArgs& a, hipStream_t s) {
+    const int n = ((a.M + BM - 1) / BM) * (a.N / BN);
+    if (n == 0) return MBERT_OK;
+    gemm_kernel<T, BM, BN, NWM, NWN, EPI, kPrefetch, OCC><<<xcd_grid(n), 64 * NWM * NWN, 0, s>>>(a);
+    MB_CHECK_LAUNCH();
+    return MBERT_OK;
+}
+
 template <typename T, int EPI>
 int run_gemm(const GemmArgs& a, hipStream_t s) {
     if ((a.K * (int)sizeof(T)) % (128 * kPrefetch) != 0) return MBERT_EUNSUPPORTED;
-    const int big = ((a.M + 255) / 256) * (a.N / 256);
-    if (a.N % 256 == 0 && big >= MB_GEMM_BIG_MIN_TILES) {
-        gemm_kernel<T, 256, 256, 2, 4, EPI, kPrefetch><<<xcd_grid(big), 512, 0, s>>>(a);
-    } else {
-        constexpr int BM = (EPI == EPI_RESID) ? 64 : 128;
-        const int n = ((a.M + BM - 1) / BM) * (a.N / 128);
-        if (n == 0) return MBERT_OK;
-        if (EPI == EPI_RESID && ((a.M + 127) / 128) * (a.N / 128) >= 1024)
-            gemm_kernel<T, 128, 128, 2, 2, EPI, kPrefetch><<<xcd_grid(((a.M + 127) / 128) * (a.N / 128)), 256, 0, s>>>(a);
-        else
-            gemm_kernel<T, BM, 128, 2, 2, EPI, kPrefetch><<<xcd_grid(n), 256, 0, s>>>(a);
-    }
-    MB_CHECK_LAUNCH();
-    return MBERT_OK;
+    const int t128 = ((a.M + 127) / 128) * (a.N / 128);
+    const int t256 = ((a.M + 255) / 256) * (a.N / 256);
+    if (a.N % 256 == 0 && t256 >= MB_GEMM_BIG_MIN_TILES)
+        return launch_tiles<T, 256, 256, 2, 4, EPI, 1>(a, s);
+    if (t128 >= MB_GEMM_SMALL_MAX_TILES) return launch_tiles<T, 128, 128, 2, 2, EPI, 2>(a, s);
+    if (a.N == D) return launch_tiles<T, 64, 64, 2, 2, EPI, 4>(a, s);
+    return launch_tiles<T, 128, 64, 2, 2, EPI, 2>(a, s);
 }
 
 template <typename T>

@@ -85,14 +85,18 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
 }
 
 // Final LayerNorm over one work tile (<= 128 rows of one sequence) plus the tile's column sums
-// of the normalised rows, reduced in a fixed order (no atomics: bitwise reproducible).
+// of the normalised rows, reduced in a fixed order (no atomics: bitwise reproducible). Sixteen
+// waves per tile keep eight rows in flight per wave.
+constexpr int FWAVES = 16;
+
 template <typename T>
-__global__ __launch_bounds__(256) void final_ln_kernel(const float* __restrict__ resid,
-                                                       const int* __restrict__ meta, int total_max,
-                                                       int S, const T* __restrict__ w, float eps,
-                                                       float* __restrict__ out,
-                                                       float* __restrict__ partials) {
-    __shared__ float red[4][D];
+__global__ __launch_bounds__(64 * FWAVES) void final_ln_kernel(const float* __restrict__ resid,
+                                                               const int* __restrict__ meta,
+                                                               int total_max, int S,
+                                                               const T* __restrict__ w, float eps,
+                                                               float* __restrict__ out,
+                                                               float* __restrict__ partials) {
+    __shared__ float red[FWAVES][D];
     const MetaView mv = meta_view(const_cast<int*>(meta), total_max, S);
     const int b = blockIdx.x;
     if (b >= mv.counts[MBERT_META_NTILES]) return;
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(256) void final_ln_kernel(const float* __restrict__
     float acc[12];
 #pragma unroll
     for (int i = 0; i < 12; ++i) acc[i] = 0.f;
-    for (int r = wave; r < tl.y; r += 4) {
+    for (int r = wave; r < tl.y; r += FWAVES) {
         const long row = tl.x + r;
         float v[12];
         load_row12(resid + row * D, lane, v);
@@ -116,8 +120,12 @@ __global__ __launch_bounds__(256) void final_ln_kernel(const float* __restrict__
 #pragma unroll
         for (int e = 0; e < 4; ++e) red[wave][4 * (lane + 64 * c) + e] = acc[4 * c + e];
     __syncthreads();
-    for (int col = threadIdx.x; col < D; col += 256)
-        partials[(long)b * D + col] = ((red[0][col] + red[1][col]) + red[2][col]) + red[3][col];
+    for (int col = threadIdx.x; col < D; col += 64 * FWAVES) {
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < FWAVES; ++q) sum += red[q][col];
+        partials[(long)b * D + col] = sum;
+    }
 }
 
 // Mean over the sequence from the tile partials (in tile order), then L2 normalisation
@@ -232,15 +240,15 @@ int launch_final_ln_pool(const float* resid, int total, const int32_t* meta, int
         float* part = pooled ? partials : nullptr;
         switch (dt) {
             case MBERT_F32:
-                final_ln_kernel<float><<<(unsigned)tmax, 256, 0, s>>>(resid, meta, total, n_seqs,
+                final_ln_kernel<float><<<(unsigned)tmax, 64 * FWAVES, 0, s>>>(resid, meta, total, n_seqs,
                                                                       (const float*)w, eps, out, part);
                 break;
             case MBERT_BF16:
-                final_ln_kernel<bf16><<<(unsigned)tmax, 256, 0, s>>>(resid, meta, total, n_seqs,
+                final_ln_kernel<bf16><<<(unsigned)tmax, 64 * FWAVES, 0, s>>>(resid, meta, total, n_seqs,
                                                                      (const bf16*)w, eps, out, part);
                 break;
             case MBERT_F16:
-                final_ln_kernel<f16><<<(unsigned)tmax, 256, 0, s>>>(resid, meta, total, n_seqs,
+                final_ln_kernel<f16><<<(unsigned)tmax, 64 * FWAVES, 0, s>>>(resid, meta, total, n_seqs,
                                                                     (const f16*)w, eps, out, part);
                 break;
             default:
