@@ -7,8 +7,9 @@
 // (64 16-bit or 32 fp32 elements). Global loads run P K-tiles ahead of the MFMAs through
 // register staging (K is only 768 or 1152, so a workgroup's whole life is a dozen K-steps and
 // the load latency has to be covered by loads in flight, not by a long loop), and feed two LDS
-// stages, one barrier per K-step. LDS rows are padded to 144 bytes so the 16-byte operand
-// reads of 8 consecutive lanes hit distinct banks.
+// stages, one barrier per K-step. LDS rows are unpadded and XOR-swizzled by 16-byte chunk (see
+// lds_off), which keeps the 16-byte operand reads conflict-free and a 128x64 tile's two stages
+// at 48 KB, three workgroups per CU.
 //
 // Epilogue: the fp32 accumulator tile is staged through LDS (row pitch BN + 8 floats, which
 // keeps the two half-waves of an MFMA block on disjoint banks) and then processed row-major,
@@ -80,6 +81,59 @@ __device__ __forceinline__ float gelu_erf(float z) {
     return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
 }
 
+// Tiles over the 8 XCDs (each with its own L2): the (row-tile, column-tile) grid is cut into
+// a x b blocks, a * b = 8, one block per XCD, so an XCD fetches only its rows of A and its
+// columns of B. The split balances tiles per XCD first, then minimises the bytes the XCDs
+// fetch between them, proportional to M/a + N/b (K is common). Within a block, consecutive
+// workgroups share rows of A.
+__host__ __device__ inline void xcd_split(int nbm, int nbn, int M, int N, int& a, int& bmper,
+                                          int& bnper) {
+    int best_tiles = 0x7fffffff;
+    long best_bytes = 0x7fffffffffffL;
+    a = NXCD;
+    for (int aa = NXCD; aa >= 1; aa >>= 1) {
+        const int bb = NXCD / aa;
+        const int tiles = ((nbm + aa - 1) / aa) * ((nbn + bb - 1) / bb);
+        const long bytes = (long)M / aa + (long)N / bb;
+        if (tiles < best_tiles || (tiles == best_tiles && bytes < best_bytes)) {
+            best_tiles = tiles;
+            best_bytes = bytes;
+            a = aa;
+        }
+    }
+    bmper = (nbm + a - 1) / a;
+    bnper = (nbn + (NXCD / a) - 1) / (NXCD / a);
+}
+
+__device__ __forceinline__ bool xcd_tile(int hw_id, int nbm, int nbn, int M, int N, int& bm,
+                                         int& bn) {
+    int a, bmper, bnper;
+    xcd_split(nbm, nbn, M, N, a, bmper, bnper);
+    const int xcd = hw_id % NXCD, local = hw_id / NXCD;
+    if (local >= bmper * bnper) return false;
+    const int b = NXCD / a;
+    bm = (xcd / b) * bmper + local / bnper;
+    bn = (xcd % b) * bnper + local % bnper;
+    return bm < nbm && bn < nbn;
+}
+
+// Grid size covering every split the device may choose for any row count up to M.
+inline int xcd_gemm_grid(int M, int BM, int N, int BN) {
+    const int nbm = (M + BM - 1) / BM, nbn = N / BN;
+    int worst = 0;
+    for (int aa = NXCD; aa >= 1; aa >>= 1) {
+        const int bb = NXCD / aa;
+        worst = max(worst, ((nbm + aa - 1) / aa) * ((nbn + bb - 1) / bb));
+    }
+    return NXCD * worst;
+}
+
+// LDS position of 16-byte chunk c (0..7) of stage row r: rows are 128 bytes, unpadded, and
+// chunk c is stored at slot c ^ ((r >> 1) & 7). Sixteen consecutive rows read at one logical
+// chunk then cover all 64 banks (rows r and r+1 differ by half the banks, pairs of rows by the
+// slot), and the eight lanes that store one row write it contiguously.
+__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
 template <int EPI, int BN>
 __device__ __forceinline__ int b_row(int bn, int r) {
     if constexpr (EPI == EPI_GEGLU) {
@@ -112,14 +166,14 @@ __device__ __forceinline__ void load8(const float* src, float* v) {
 template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int P, int OCC>
 __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     constexpr int NT = 64 * NWM * NWN;                    // threads
-    constexpr int ROWB = 128, PITCH = 144;
+    constexpr int ROWB = 128;  // bytes of K per row per stage; rows are unpadded (swizzled)
     constexpr int KT = ROWB / (int)sizeof(T);
     constexpr int WM = BM / NWM, WN = BN / NWN, FM = WM / 32, FN = WN / 32;
     constexpr int RSTEP = NT / 8;                         // rows per 16-byte-chunk pass
     constexpr int ACH = BM / RSTEP, BCH = BN / RSTEP;
     constexpr int CP = BN + 8;                            // epilogue staging pitch (floats)
     constexpr int EROWS = NWM * 32;                       // rows staged per epilogue pass
-    constexpr int MAIN_BYTES = 2 * (BM + BN) * PITCH;
+    constexpr int MAIN_BYTES = 2 * (BM + BN) * ROWB;
     constexpr int EPI_BYTES = EROWS * CP * 4;
     constexpr int SMEM = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
     static_assert(EPI != EPI_ROPE || BN % 64 == 0, "RoPE tiles hold whole heads");
@@ -128,13 +182,8 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
 
     const int nbn = p.N / BN;
     const int M = rows_of(p.counts, p.M);
-    const int n_act = ((M + BM - 1) / BM) * nbn;
-    const int per = (n_act + NXCD - 1) / NXCD;
-    const int local = blockIdx.x / NXCD;
-    if (local >= per) return;
-    const int tile = (blockIdx.x % NXCD) * per + local;
-    if (tile >= n_act) return;
-    const int bm = tile / nbn, bn = tile % nbn;
+    int bm, bn;
+    if (!xcd_tile(blockIdx.x, (M + BM - 1) / BM, nbn, M, p.N, bm, bn)) return;
     const int m0 = bm * BM;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -165,7 +214,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     const int nk = p.K / KT;
-    const int lrow = lane & 31, lk = (lane >> 5) * 16;
+    const int lrow = lane & 31, lk = lane >> 5;  // lk: which 16-byte half of a 32-byte k-step
 
 #define MB_GLOAD(KT_, U_)                                                                 \
     do {                                                                                  \
@@ -175,11 +224,11 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     } while (0)
 #define MB_SSTORE(U_, ST_)                                                                \
     do {                                                                                  \
-        unsigned char* base_ = smem + (ST_) * (BM + BN) * PITCH;                          \
+        unsigned char* base_ = smem + (ST_) * (BM + BN) * ROWB;                           \
         _Pragma("unroll") for (int i = 0; i < ACH; ++i)                                   \
-            *(u32x4*)(base_ + (crow + RSTEP * i) * PITCH + cchunk * 16) = ra[U_][i];      \
+            *(u32x4*)(base_ + lds_off(crow + RSTEP * i, cchunk)) = ra[U_][i];             \
         _Pragma("unroll") for (int i = 0; i < BCH; ++i)                                   \
-            *(u32x4*)(base_ + (BM + crow + RSTEP * i) * PITCH + cchunk * 16) = rb[U_][i]; \
+            *(u32x4*)(base_ + lds_off(BM + crow + RSTEP * i, cchunk)) = rb[U_][i];        \
     } while (0)
 
     // Every load is unconditional (the tail re-reads the last K-tile, whose data is never
@@ -196,17 +245,16 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
             const int kt = kt0 + u;
             MB_GLOAD(min(kt + P, nk - 1), u);
             __builtin_amdgcn_sched_barrier(0);  // keep the prefetch at the head of the K-step
-            const unsigned char* As = smem + (kt & 1) * (BM + BN) * PITCH;
-            const unsigned char* Bs = As + BM * PITCH;
+            const unsigned char* St = smem + (kt & 1) * (BM + BN) * ROWB;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 u32x4 af[FM], bf[FN];
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
-                    af[i] = *(const u32x4*)(As + (wm * WM + 32 * i + lrow) * PITCH + s * 32 + lk);
+                    af[i] = *(const u32x4*)(St + lds_off(wm * WM + 32 * i + lrow, 2 * s + lk));
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    bf[j] = *(const u32x4*)(Bs + (wn * WN + 32 * j + lrow) * PITCH + s * 32 + lk);
+                    bf[j] = *(const u32x4*)(St + lds_off(BM + wn * WN + 32 * j + lrow, 2 * s + lk));
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -321,7 +369,8 @@ template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int OCC>
 int launch_tiles(const GemmArgs& a, hipStream_t s) {
     const int n = ((a.M + BM - 1) / BM) * (a.N / BN);
     if (n == 0) return MBERT_OK;
-    gemm_kernel<T, BM, BN, NWM, NWN, EPI, kPrefetch, OCC><<<xcd_grid(n), 64 * NWM * NWN, 0, s>>>(a);
+    gemm_kernel<T, BM, BN, NWM, NWN, EPI, kPrefetch, OCC>
+        <<<xcd_gemm_grid(a.M, BM, a.N, BN), 64 * NWM * NWN, 0, s>>>(a);
     MB_CHECK_LAUNCH();
     return MBERT_OK;
 }
@@ -335,7 +384,7 @@ int run_gemm(const GemmArgs& a, hipStream_t s) {
         return launch_tiles<T, 256, 256, 2, 4, EPI, 1>(a, s);
     if (t128 >= MB_GEMM_SMALL_MAX_TILES) return launch_tiles<T, 128, 128, 2, 2, EPI, 2>(a, s);
     if (a.N == D) return launch_tiles<T, 64, 64, 2, 2, EPI, 4>(a, s);
-    return launch_tiles<T, 128, 64, 2, 2, EPI, 2>(a, s);
+    return launch_tiles<T, 128, 64, 2, 2, EPI, 3>(a, s);
 }
 
 template <typename T>
