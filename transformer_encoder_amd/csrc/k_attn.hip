@@ -17,7 +17,9 @@
 // V is stored transposed in LDS ([d][key]) so each lane's 8 keys are two 8-byte reads. The
 // MFMA k-slots of both operands follow the same key permutation (lane group g holds keys
 // 4g..4g+3 and 8+4g..8+4g+3 of each 16-key slice), which leaves the product unchanged.
-// Softmax is online in fp32 with exp2 and the scale 0.125 * log2(e) folded into one multiply.
+// Softmax is online in fp32 with exp2 and the scale 0.125 * log2(e) folded into one FMA; edge
+// tiles are masked branch-free; the running max is only raised (and the output rescaled) when a
+// row's max grows by more than 2^8.
 // The fp32 variant uses v_mfma_f32_32x32x2_f32 and keeps V in natural layout.
 #include "common.hpp"
 
@@ -203,39 +205,54 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
                     }
                 }
             }
-            // ---- online softmax (per lane = per query)
+            // ---- online softmax (per lane = per query), branch-free masking
             const bool need_mask = is_global ? (kb + 63 > khi) : !(kb >= all_lo && kb + 63 <= all_hi);
             float sv[32];
             float mx = -INFINITY;
+            if (need_mask) {
+                // key of element e = kb + 4g + [32kk + 8(e/4) + (e%4)]; compare the constant part
+                const int lo_rel = qlo - (kb + 4 * g), hi_rel = qhi - (kb + 4 * g);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int rel = 32 * kk + 8 * (e >> 2) + (e & 3);
+                        const float x = (rel >= lo_rel && rel <= hi_rel) ? sacc[kk][e] : -INFINITY;
+                        sv[16 * kk + e] = x;
+                        mx = fmaxf(mx, x);
+                    }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        sv[16 * kk + e] = sacc[kk][e];
+                        mx = fmaxf(mx, sacc[kk][e]);
+                    }
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;  // row max, log2 units
+            // Lazy rescale: the running max only moves (and O, l are rescaled) when some lane's
+            // row max exceeds it by more than 8; otherwise exp2 arguments stay <= 8 (p <= 256).
+            // Softmax is invariant to the subtracted constant, so the result is the same.
+            if (__any(mx > m_run + 8.0f)) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    float x = sacc[kk][e] * scale_log2;
-                    if (need_mask) {
-                        const int key = kb + 32 * kk + 8 * (e >> 2) + 4 * g + (e & 3);
-                        if (key < qlo || key > qhi) x = -INFINITY;
-                    }
-                    sv[16 * kk + e] = x;
-                    mx = fmaxf(mx, x);
+                    oacc[0][e] *= alpha;
+                    oacc[1][e] *= alpha;
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+                m_run = m_new;
+            }
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
             float lsum = 0.f;
 #pragma unroll
             for (int i = 0; i < 32; ++i) {
-                sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
+                sv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], scale_log2, -m_use));
                 lsum += sv[i];
             }
-            l_run = l_run * alpha + lsum;
-            m_run = m_new;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                oacc[0][e] *= alpha;
-                oacc[1][e] *= alpha;
-            }
+            l_run += lsum;
             // ---- O^T += V^T P^T
             if constexpr (F32) {
 #pragma unroll
