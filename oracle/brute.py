@@ -118,3 +118,20 @@ def encode(ids, cu_seqlens, weights, *, n_layers, hidden, n_heads, head_dim, int
         nrm = math.sqrt(sum(m * m for m in mean))
         pooled.append([m / max(nrm, 1e-12) for m in mean])
     return out, pooled
+
+
+def prediction_head(x, W_dense, norm_w, eps):
+    """Dense (no bias), GELU, LayerNorm of one vector (kgptalkie, §"The Masked-LM Head")."""
+    return _ln([_gelu(u) for u in _matvec(W_dense, x)], norm_w, eps)
+
+
+def mlm_logits(x, W_dense, norm_w, tok_emb, decoder_bias, eps):
+    """Scores of one vector against every vocabulary row (tied decoder, with bias)."""
+    h = prediction_head(x, W_dense, norm_w, eps)
+    return [sum(e[j] * h[j] for j in range(len(h))) + decoder_bias[v] for v, e in enumerate(tok_emb)]
+
+
+def classifier_logits(pooled, W_dense, norm_w, W_cls, b_cls, eps):
+    """Scores of one pooled vector per label (kgptalkie, §"How Do We Put a Classifier on Top?")."""
+    h = prediction_head(pooled, W_dense, norm_w, eps)
+    return [sum(Wc[j] * h[j] for j in range(len(h))) + b_cls[c] for c, Wc in enumerate(W_cls)]

@@ -408,3 +408,74 @@ def repad(out, indices, B: int, Tp: int) -> np.ndarray:
     res = np.zeros((B * Tp, out.shape[1]), dtype=np.float64)
     res[np.asarray(indices, dtype=np.int64)] = out
     return res.reshape(B, Tp, out.shape[1])
+
+
+# ---------------------------------------------------------------------------- heads and pooling
+# The masked-LM and classification heads on top of the encoder ([KGP] §"The Masked-LM Head",
+# §"How Do We Put a Classifier on Top?"): both start with the same prediction head, a Linear
+# 768 -> 768 without bias, GELU, and a LayerNorm. The model's other LayerNorms carry no bias
+# and the page's printout of this one names none; it is read as weight-only like the rest.
+
+def prediction_head(x, W_dense, norm_w, eps: float) -> np.ndarray:
+    """LN(gelu_erf(x W_dense^T); norm_w) ([KGP] §"The Masked-LM Head": dense, GELU, LayerNorm)."""
+    u = np.asarray(x, dtype=np.float64) @ np.asarray(W_dense, dtype=np.float64).T
+    return layernorm(gelu_erf(u), norm_w, eps)
+
+
+def mlm_logits(x, W_dense, norm_w, tok_emb, decoder_bias, eps: float) -> np.ndarray:
+    """Vocabulary scores: the prediction head, then the decoder, whose weight is the embedding
+    table itself (weight tying) and which carries a bias ([KGP] §"The Masked-LM Head")."""
+    h = prediction_head(x, W_dense, norm_w, eps)
+    return h @ np.asarray(tok_emb, dtype=np.float64).T + np.asarray(decoder_bias, dtype=np.float64)
+
+
+def mean_pool(out, cu_seqlens) -> np.ndarray:
+    """Mean over each sequence's rows, not normalised (the pooling the classifier reads,
+    [KGP] §"How Do We Get One Vector per Text?", §"How Do We Put a Classifier on Top?").
+    An empty sequence pools to zero."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    out = np.asarray(out, dtype=np.float64)
+    pooled = np.zeros((len(cu) - 1, out.shape[1]), dtype=np.float64)
+    for s in range(len(cu) - 1):
+        if cu[s + 1] > cu[s]:
+            pooled[s] = out[cu[s]:cu[s + 1]].mean(axis=0)
+    return pooled
+
+
+def cls_pool(out, cu_seqlens) -> np.ndarray:
+    """The first row of each sequence (CLS pooling, index 0: [CAN] §"Pooling and
+    normalization"). An empty sequence pools to zero."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    out = np.asarray(out, dtype=np.float64)
+    pooled = np.zeros((len(cu) - 1, out.shape[1]), dtype=np.float64)
+    for s in range(len(cu) - 1):
+        if cu[s + 1] > cu[s]:
+            pooled[s] = out[cu[s]]
+    return pooled
+
+
+def l2_normalize(v, l2_eps: float = 1e-12) -> np.ndarray:
+    """Each row divided by max(its L2 norm, eps) ([SBD] §"Implementing it": normalize)."""
+    v = np.asarray(v, dtype=np.float64)
+    n = np.sqrt((v * v).sum(axis=-1, keepdims=True))
+    return v / np.maximum(n, l2_eps)
+
+
+def classifier_logits(pooled, W_dense, norm_w, W_cls, b_cls, eps: float) -> np.ndarray:
+    """Scores per label: the prediction head on the pooled vector, then a Linear with bias,
+    one output per label ([KGP] §"How Do We Put a Classifier on Top?")."""
+    h = prediction_head(pooled, W_dense, norm_w, eps)
+    return h @ np.asarray(W_cls, dtype=np.float64).T + np.asarray(b_cls, dtype=np.float64)
+
+
+def class_probabilities(logits) -> np.ndarray:
+    """Softmax over the labels ([KGP] §"How Do We Put a Classifier on Top?")."""
+    z = np.asarray(logits, dtype=np.float64)
+    e = np.exp(z - z.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def cross_entropy(logits, label: int) -> float:
+    """Minus the log of the probability of the true label ([KGP] §"How Do We Put a Classifier
+    on Top?": the loss is minus the log of that probability)."""
+    return float(-np.log(class_probabilities(logits)[label]))
