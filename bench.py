@@ -191,6 +191,61 @@ def cpu_baseline(wl, weights, batch, budget_s=12.0):
                       f"{t_used:.1f} s"}
 
 
+def measure_heads(B, m, wl, ws, rows_ptr, total_max, T, S, stream, steps):
+    """Pooling and the two heads on the forward's own output rows, outside the timed forward
+    (kgptalkie, "The Masked-LM Head", "How Do We Put a Classifier on Top?"; candding, "Pooling
+    and normalization"): the masked-LM head over every real position, CLS and mean pooling,
+    and the 4-label classifier head on mean pooling. `rows_ptr` is the packed fp32 output
+    [T, 768]; the workspace still holds the meta buffer. Each is timed with HIP events on the
+    stream, averaged over `steps` calls."""
+    import torch
+    from workloads import Dims, make_head_weights
+    from transformer_encoder_amd.model import to_device
+    dt = B.DTYPES[wl.dtype]
+    hw = make_head_weights(Dims(n_layers=wl.n_layers), wl.dtype, wl.id)
+    w = {k: to_device(v, wl.dtype, "cuda") for k, v in hw.items()}
+    L = m.layout(total_max, S)
+    meta, parts = ws.data_ptr() + L.meta, ws.data_ptr() + L.partials
+    vocab = int(m.cfg.vocab)
+    hws_n = B.mbert_head_workspace_bytes(dt, T)
+    hws = torch.empty(hws_n, dtype=torch.uint8, device="cuda")
+    logits = torch.empty((T, vocab), dtype=torch.float32, device="cuda")
+    pooled = torch.empty((S, D), dtype=torch.float32, device="cuda")
+    cls_logits = torch.empty((S, 4), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    calls = {
+        "mlm_head_all_positions": lambda: B.mbert_mlm_head(
+            dt, rows_ptr, T, None, T, w["dense"], w["norm"], 1e-5, m.tok_emb, w["decoder_bias"],
+            vocab, hws, hws_n, logits, stream),
+        "pool_cls_l2": lambda: B.mbert_pool(rows_ptr, total_max, meta, S, B.POOL_CLS | B.POOL_L2,
+                                            pooled, parts, stream),
+        "pool_mean": lambda: B.mbert_pool(rows_ptr, total_max, meta, S, B.POOL_MEAN, pooled, parts,
+                                          stream),
+        "classifier_head_4_labels": lambda: B.mbert_classifier_head(
+            dt, pooled, S, w["dense"], w["norm"], 1e-5, w["cls_W"], w["cls_b"], 4, hws, hws_n,
+            cls_logits, stream),
+    }
+    res = {"rows": T, "vocab": vocab}
+    for name, fn in calls.items():
+        fn()
+        stream.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        stream.synchronize()
+        res[name] = {"ms": round(e0.elapsed_time(e1) / steps, 5)}
+    mlm = res["mlm_head_all_positions"]
+    flops = 2.0 * T * D * (D + vocab)
+    mlm["algorithmic_tflop"] = round(flops / 1e12, 4)
+    mlm["tflops"] = round(flops / (mlm["ms"] * 1e-3) / 1e12, 1)
+    mlm["mfma_peak_frac"] = round(flops / (mlm["ms"] * 1e-3) / 1e12 / PEAK_MFMA_16BIT, 4) \
+        if wl.dtype != "f32" else None
+    mlm["logits_write_gb_s"] = round(T * vocab * 4 / (mlm["ms"] * 1e-3) / 1e9, 1)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +254,7 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of the graph")
+    ap.add_argument("--no-heads", action="store_true", help="skip the pooling and head timings")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_<kind>_<workload>.{json,md} from two "
                          "rocprofv3 --pmc runs of this script and exit")
@@ -320,6 +376,15 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
+    heads = None
+    if not args.no_heads:
+        # the last eager forward's packed rows: the workspace's out region (padded batch) or
+        # the caller's out (packed batch)
+        total_max = Bn * Tp if padded else T
+        rows_ptr = ws.data_ptr() + m.layout(total_max, S).out if padded else out.data_ptr()
+        heads = measure_heads(B, m, wl, ws, rows_ptr, total_max, T, S, stream,
+                              min(args.steps, 20))
+
     ms = eager_ms if args.eager else graph_ms
     tokens_per_s = T / (ms * 1e-3)
     pairs_g = attention_pairs(lengths, True)
@@ -366,6 +431,8 @@ def main():
                      "avg_launch_ms": round(dom_avg_ms, 5),
                      "work_per_launch": work},
     }
+    if heads is not None:
+        line["heads"] = heads
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, weights, batch)
     print(json.dumps(line), flush=True)

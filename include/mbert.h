@@ -209,6 +209,38 @@ int mbert_final_ln_pool(const float* resid, int total, const int32_t* meta, int 
                         mbert_dtype dtype, const void* w, float eps, float* out,
                         float* pooled, float* partials, void* stream);
 
+/* Pooling of finished rows out [T,768] f32 (after the final LayerNorm), per sequence of the
+ * meta buffer: MBERT_POOL_MEAN, the mean of the sequence's rows (kgptalkie §"How Do We Get
+ * One Vector per Text?"), or MBERT_POOL_CLS, its first row (candding §"Pooling and
+ * normalization": index 0); with MBERT_POOL_L2 or'ed in, each pooled vector is divided by
+ * max(L2 norm, 1e-12). An empty sequence pools to 0. `partials` is scratch of
+ * mbert_pool_partial_floats(total, n_seqs) floats (unused, may be NULL, for CLS). Deterministic. */
+enum { MBERT_POOL_MEAN = 0, MBERT_POOL_CLS = 1, MBERT_POOL_L2 = 2 };
+int mbert_pool(const float* out, int total, const int32_t* meta, int n_seqs, int mode,
+               float* pooled, float* partials, void* stream);
+
+/* ---- heads (kgptalkie §"The Masked-LM Head", §"How Do We Put a Classifier on Top?")
+ * Both start with the prediction head: h = LN(gelu_erf(x . W_dense^T); norm_w, eps), W_dense
+ * [768,768] without bias, LayerNorm weight-only like the encoder's.
+ * mbert_mlm_head: x is the final hidden state [total,768] f32; rows (device int32 [n_rows], or
+ * NULL for rows 0..n_rows-1) selects the positions to score (e.g. the [MASK] tokens); a row
+ * index outside [0, total) scores a zero vector. logits [n_rows, vocab] f32 = h . decoder_w^T
+ * + decoder_b, decoder_w [vocab,768] (the tied embedding table), decoder_b [vocab]; vocab must
+ * be a multiple of 64 (50,368 is).
+ * mbert_classifier_head: pooled [n_seqs,768] f32 (mbert_pool, MBERT_POOL_MEAN without L2 for
+ * ModernBERT's classifier); logits [n_seqs, n_labels] f32 = h . W_cls^T + b_cls, W_cls
+ * [n_labels,768], b_cls [n_labels], 1 <= n_labels <= 4096.
+ * Weights are of `dtype`. `ws` is device scratch of mbert_head_workspace_bytes(dtype, rows)
+ * bytes, rows = n_rows or n_seqs. */
+size_t mbert_head_workspace_bytes(mbert_dtype dtype, int rows);
+int mbert_mlm_head(mbert_dtype dtype, const float* x, int total, const int32_t* rows, int n_rows,
+                   const void* W_dense, const void* norm_w, float eps, const void* decoder_w,
+                   const void* decoder_b, int vocab, void* ws, size_t ws_bytes, float* logits,
+                   void* stream);
+int mbert_classifier_head(mbert_dtype dtype, const float* pooled, int n_seqs, const void* W_dense,
+                          const void* norm_w, float eps, const void* W_cls, const void* b_cls,
+                          int n_labels, void* ws, size_t ws_bytes, float* logits, void* stream);
+
 /* Re-pad: out_pad [B,Tpad,768] f32 gets row rowmap[b*Tpad+t] of out, or zeros where
  * rowmap is -1 (the zero-filled unpacking of rayaq §"Padding and the key padding mask"). */
 int mbert_repad(const float* out, const int32_t* rowmap, int B, int Tpad, float* out_pad,

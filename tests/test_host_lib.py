@@ -66,6 +66,14 @@ def test_strerror_and_sizes():
     assert [B.mbert_dtype_size(d) for d in (0, 1, 2, 7)] == [4, 2, 2, 0]
 
 
+def test_head_workspace_bytes():
+    for dt, ds in ((B.MBERT_F32, 4), (B.MBERT_BF16, 2), (B.MBERT_F16, 2)):
+        for R in (0, 1, 7, 2445):
+            n = B.mbert_head_workspace_bytes(dt, R)
+            assert n >= R * 768 * (2 * ds + 4) and n % 256 == 0
+    assert B.mbert_head_workspace_bytes(9, 4) == 0
+
+
 def test_meta_and_workspace_layout():
     c = B.mbert_default_config()
     for T, S in ((0, 0), (1, 1), (300, 1), (2445, 8), (262144, 32)):
@@ -138,4 +146,22 @@ def test_step_validation_paths(lib):
     assert lib.mbert_unpad(fake, fake, -1, 5, 8192, fake, fake, fake, fake, fake, None) == B.MBERT_EINVAL
     assert lib.mbert_final_ln_pool(fake, 10, fake, 1, 1, fake, 1e-5, fake, fake, None, None) == B.MBERT_EINVAL
     assert lib.mbert_graph_launch(None, None) == B.MBERT_EINVAL
+    # pooling and heads
+    assert lib.mbert_pool(fake, 10, fake, 1, 4, fake, fake, None) == B.MBERT_EINVAL
+    assert lib.mbert_pool(fake, 10, None, 1, 0, fake, fake, None) == B.MBERT_EINVAL
+    assert lib.mbert_pool(fake, 10, fake, 1, B.POOL_MEAN, fake, None, None) == B.MBERT_EINVAL
+    mlm = lib.mbert_mlm_head
+    assert mlm(1, fake, 10, None, 4, fake, fake, 1e-5, fake, fake, 50000, fake, 1 << 30, fake,
+               None) == B.MBERT_EUNSUPPORTED  # vocabulary not a multiple of 64
+    assert mlm(1, fake, 10, None, 11, fake, fake, 1e-5, fake, fake, 64, fake, 1 << 30, fake,
+               None) == B.MBERT_EINVAL  # more rows than positions without a row list
+    need = B.mbert_head_workspace_bytes(B.MBERT_BF16, 4)
+    assert mlm(1, fake, 10, None, 4, fake, fake, 1e-5, fake, fake, 64, fake, need - 1, fake,
+               None) == B.MBERT_ENOSPC
+    assert mlm(7, fake, 10, None, 4, fake, fake, 1e-5, fake, fake, 64, fake, need, fake,
+               None) == B.MBERT_EUNSUPPORTED
+    clf = lib.mbert_classifier_head
+    assert clf(1, fake, 4, fake, fake, 1e-5, fake, fake, 0, fake, need, fake, None) == B.MBERT_EINVAL
+    assert clf(1, fake, 4, fake, fake, 1e-5, fake, fake, 4, fake, need - 1, fake, None) == B.MBERT_ENOSPC
+    assert clf(1, fake, 0, None, None, 1e-5, None, None, 4, None, 0, None, None) == B.MBERT_OK
     assert lib.mbert_timer_create(0, ctypes.byref(ctypes.c_void_p())) == B.MBERT_EINVAL

@@ -19,6 +19,7 @@ MBERT_OK, MBERT_EINVAL, MBERT_EUNSUPPORTED, MBERT_ERANGE, MBERT_ENOSPC, MBERT_EH
 MBERT_F32, MBERT_BF16, MBERT_F16 = 0, 1, 2
 DTYPES = {"f32": MBERT_F32, "bf16": MBERT_BF16, "f16": MBERT_F16}
 STATUS_BAD_CU, STATUS_TOO_LONG, STATUS_BAD_MASK, STATUS_BAD_ID = 1, 2, 4, 8
+POOL_MEAN, POOL_CLS, POOL_L2 = 0, 1, 2
 (K_EMBED_LN, K_LAYERNORM, K_QKV_ROPE, K_ATTN_GLOBAL, K_ATTN_LOCAL, K_WO_RESID, K_WI_GEGLU,
  K_WO2_RESID, K_FINAL_POOL, K_META) = range(10)
 KERNEL_KINDS = {"embed_ln": 0, "layernorm": 1, "qkv_rope": 2, "attn_global": 3, "attn_local": 4,
@@ -79,6 +80,10 @@ _SIGNATURES = {
     "mbert_pool_partial_floats": ([I, I], SZ),
     "mbert_final_ln_pool": ([P, I, P, I, I, P, c_float, P, P, P, P], I),
     "mbert_repad": ([P, P, I, I, P, P], I),
+    "mbert_pool": ([P, I, P, I, I, P, P, P], I),
+    "mbert_head_workspace_bytes": ([I, I], SZ),
+    "mbert_mlm_head": ([I, P, I, P, I, P, P, c_float, P, P, I, P, SZ, P, P], I),
+    "mbert_classifier_head": ([I, P, I, P, P, c_float, P, P, I, P, SZ, P, P], I),
     "mbert_workspace_bytes": ([POINTER(mbert_config), I, I, I], SZ),
     "mbert_workspace_layout": ([POINTER(mbert_config), I, I, I, POINTER(mbert_ws_layout)], I),
     "mbert_layer": ([POINTER(mbert_weights), I, I, I, P, SZ, P], I),
@@ -256,6 +261,28 @@ def mbert_final_ln_pool(resid, total, meta, n_seqs, dtype, w, eps, out, pooled, 
                         stream=None):
     _call("mbert_final_ln_pool", ptr(resid), total, ptr(meta), n_seqs, dtype, ptr(w), eps,
           ptr(out), ptr(pooled), ptr(partials), stream_handle(stream))
+
+
+def mbert_pool(out, total, meta, n_seqs, mode, pooled, partials=None, stream=None):
+    _call("mbert_pool", ptr(out), total, ptr(meta), n_seqs, mode, ptr(pooled), ptr(partials),
+          stream_handle(stream))
+
+
+def mbert_head_workspace_bytes(dtype, rows) -> int:
+    return lib().mbert_head_workspace_bytes(dtype, rows)
+
+
+def mbert_mlm_head(dtype, x, total, rows, n_rows, W_dense, norm_w, eps, decoder_w, decoder_b,
+                   vocab, ws, ws_bytes, logits, stream=None):
+    _call("mbert_mlm_head", dtype, ptr(x), total, ptr(rows), n_rows, ptr(W_dense), ptr(norm_w),
+          eps, ptr(decoder_w), ptr(decoder_b), vocab, ptr(ws), ws_bytes, ptr(logits),
+          stream_handle(stream))
+
+
+def mbert_classifier_head(dtype, pooled, n_seqs, W_dense, norm_w, eps, W_cls, b_cls, n_labels,
+                          ws, ws_bytes, logits, stream=None):
+    _call("mbert_classifier_head", dtype, ptr(pooled), n_seqs, ptr(W_dense), ptr(norm_w), eps,
+          ptr(W_cls), ptr(b_cls), n_labels, ptr(ws), ws_bytes, ptr(logits), stream_handle(stream))
 
 
 def mbert_repad(out, rowmap, B, Tpad, out_pad, stream=None):

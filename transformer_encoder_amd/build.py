@@ -15,7 +15,7 @@ INCLUDE = ROOT / "include"
 BUILD = PKG / "_build"
 LIB = PKG / "libmbert.so"
 
-SOURCES = ["api.hip", "k_meta.hip", "k_norm.hip", "k_gemm.hip", "k_attn.hip"]
+SOURCES = ["api.hip", "k_meta.hip", "k_norm.hip", "k_gemm.hip", "k_attn.hip", "k_head.hip"]
 
 # Packed-fp32 VALU ops are disabled for all device code (-packed-fp32-ops).
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

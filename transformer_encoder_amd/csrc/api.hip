@@ -393,6 +393,81 @@ int mbert_final_ln_pool(const float* resid, int total, const int32_t* meta, int 
                                      as_stream(stream));
 }
 
+int mbert_pool(const float* out, int total, const int32_t* meta, int n_seqs, int mode,
+               float* pooled, float* partials, void* stream) {
+    MB_TRY(check_sizes(total, n_seqs));
+    if (mode < 0 || mode > 3) return MBERT_EINVAL;
+    if (n_seqs > 0 && (!meta || !pooled || (total > 0 && !out))) return MBERT_EINVAL;
+    if (n_seqs > 0 && (mode & 1) == MBERT_POOL_MEAN && !partials) return MBERT_EINVAL;
+    return mbh::launch_pool(out, total, meta, n_seqs, mode, pooled, partials, as_stream(stream));
+}
+
+namespace {
+struct HeadLayout {
+    size_t h0, u, h2, total;
+};
+HeadLayout head_layout(mbert_dtype dt, int rows) {
+    const size_t R = (size_t)(rows > 0 ? rows : 0), ds = dsize(dt);
+    HeadLayout L{};
+    L.h0 = 0;
+    L.u = align256(R * D * ds);
+    L.h2 = align256(L.u + R * D * 4);
+    L.total = align256(L.h2 + R * D * ds);
+    return L;
+}
+// h2 = LN(gelu(cast(x[rows]) . W_dense^T); norm_w): the prediction head, in the workspace.
+int prediction_head(mbert_dtype dt, const float* x, int total, const int32_t* rows, int R,
+                    const void* Wd, const void* nw, float eps, char* ws, const HeadLayout& L,
+                    hipStream_t s) {
+    MB_TRY(mbh::launch_gather_cast(dt, x, total, rows, R, ws + L.h0, s));
+    MB_TRY(mbh::launch_linear_f32(dt, ws + L.h0, R, Wd, D, D, 1, nullptr,
+                                  reinterpret_cast<float*>(ws + L.u), s));
+    return mbh::launch_layernorm(dt, reinterpret_cast<float*>(ws + L.u), R, nullptr, nw, eps,
+                                 ws + L.h2, s);
+}
+}  // namespace
+
+size_t mbert_head_workspace_bytes(mbert_dtype dt, int rows) {
+    if (check_dtype(dt) != MBERT_OK || rows < 0) return 0;
+    return head_layout(dt, rows).total;
+}
+
+int mbert_mlm_head(mbert_dtype dt, const float* x, int total, const int32_t* rows, int n_rows,
+                   const void* W_dense, const void* norm_w, float eps, const void* decoder_w,
+                   const void* decoder_b, int vocab, void* ws, size_t ws_bytes, float* logits,
+                   void* stream) {
+    MB_TRY(check_dtype(dt));
+    MB_TRY(check_sizes(total, 0));
+    if (n_rows < 0 || vocab <= 0) return MBERT_EINVAL;
+    if (vocab % 64 != 0) return MBERT_EUNSUPPORTED;
+    MB_TRY(check_sizes(n_rows, 0));
+    if (n_rows == 0) return MBERT_OK;
+    if (!x || !W_dense || !norm_w || !decoder_w || !decoder_b || !ws || !logits) return MBERT_EINVAL;
+    if (!rows && n_rows > total) return MBERT_EINVAL;
+    const HeadLayout L = head_layout(dt, n_rows);
+    if (ws_bytes < L.total) return MBERT_ENOSPC;
+    const hipStream_t s = as_stream(stream);
+    char* w = static_cast<char*>(ws);
+    MB_TRY(prediction_head(dt, x, total, rows, n_rows, W_dense, norm_w, eps, w, L, s));
+    return mbh::launch_linear_f32(dt, w + L.h2, n_rows, decoder_w, vocab, D, 0, decoder_b, logits, s);
+}
+
+int mbert_classifier_head(mbert_dtype dt, const float* pooled, int n_seqs, const void* W_dense,
+                          const void* norm_w, float eps, const void* W_cls, const void* b_cls,
+                          int n_labels, void* ws, size_t ws_bytes, float* logits, void* stream) {
+    MB_TRY(check_dtype(dt));
+    if (n_seqs < 0 || n_labels < 1 || n_labels > 4096) return MBERT_EINVAL;
+    if (n_seqs > kMaxRows) return MBERT_ERANGE;
+    if (n_seqs == 0) return MBERT_OK;
+    if (!pooled || !W_dense || !norm_w || !W_cls || !b_cls || !ws || !logits) return MBERT_EINVAL;
+    const HeadLayout L = head_layout(dt, n_seqs);
+    if (ws_bytes < L.total) return MBERT_ENOSPC;
+    const hipStream_t s = as_stream(stream);
+    char* w = static_cast<char*>(ws);
+    MB_TRY(prediction_head(dt, pooled, n_seqs, nullptr, n_seqs, W_dense, norm_w, eps, w, L, s));
+    return mbh::launch_small_linear(dt, w + L.h2, W_cls, b_cls, n_seqs, n_labels, logits, s);
+}
+
 int mbert_repad(const float* out, const int32_t* rowmap, int B, int Tpad, float* out_pad,
                 void* stream) {
     if (B < 0 || Tpad < 0) return MBERT_EINVAL;

@@ -61,10 +61,24 @@ template <> struct Vec4<f16> {
 };
 
 // ---------------------------------------------------------------- wave reductions (wave64)
+// Sum over the 64 lanes, the same value in every lane, in a fixed order. Within each row of
+// 16 lanes the data-parallel-primitive (DPP) lane swaps run on the VALU: swap neighbours, swap
+// pairs, mirror within 8, mirror within 16; the four row sums are then read as scalars and
+// added in row order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f<0x141>(v);  // row_half_mirror
+    v += dpp_f<0x140>(v);  // row_mirror
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return ((r0 + r1) + r2) + r3;
 }
 
 // ---------------------------------------------------------------- work distribution
@@ -147,6 +161,16 @@ int launch_embed_ln(mbert_dtype dt, const int32_t* ids, int total, const int32_t
                     hipStream_t s);
 int launch_layernorm(mbert_dtype dt, const float* x, int total, const int32_t* meta,
                      const void* w, float eps, void* y, hipStream_t s);
+// Pooling of finished rows: mode = MBERT_POOL_MEAN or MBERT_POOL_CLS, | MBERT_POOL_L2.
+int launch_pool(const float* out, int total, const int32_t* meta, int n_seqs, int mode,
+                float* pooled, float* partials, hipStream_t s);
+// out (fp32 [M, N]) = gelu(a . W^T) (gelu != 0) or a . W^T + bias; K = 768, N % 64 == 0.
+int launch_linear_f32(mbert_dtype dt, const void* a, int M, const void* W, int N, int K, int gelu,
+                      const void* bias, float* out, hipStream_t s);
+int launch_gather_cast(mbert_dtype dt, const float* x, int total, const int32_t* rows, int R,
+                       void* out, hipStream_t s);
+int launch_small_linear(mbert_dtype dt, const void* h, const void* W, const void* b, int S, int C,
+                        float* out, hipStream_t s);
 int launch_final_ln_pool(const float* resid, int total, const int32_t* meta, int n_seqs,
                          mbert_dtype dt, const void* w, float eps, float* out, float* pooled,
                          float* partials, hipStream_t s);

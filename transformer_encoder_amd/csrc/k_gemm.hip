@@ -23,6 +23,9 @@
 //   GEGLU : m = gelu_erf(u_gate) * u_mult; the B tile takes BN/2 rows from the GELU-branch
 //           half of Wi and the same BN/2 rows of the multiplier half, so the pair of every
 //           output column sits in one tile (candding, §"The feed-forward halves").
+//   GELU_F32 / BIAS_F32 : C (fp32, row pitch N) = gelu_erf(acc) or acc + bias[col], the dense
+//           layer of the prediction head and the biased decoder / classifier Linear
+//           (kgptalkie, §"The Masked-LM Head")
 // Work distribution: tiles are spread over the 8 XCDs in contiguous ranges counted from the
 // real row count read on the device (the padded path sizes its grid for B * Tpad rows).
 #include "common.hpp"
@@ -36,7 +39,7 @@
 
 namespace mb {
 
-enum { EPI_STORE = 0, EPI_ROPE = 1, EPI_RESID = 2, EPI_GEGLU = 3 };
+enum { EPI_STORE = 0, EPI_ROPE = 1, EPI_RESID = 2, EPI_GEGLU = 3, EPI_GELU_F32 = 4, EPI_BIAS_F32 = 5 };
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -51,6 +54,7 @@ struct GemmArgs {
     const int* pos;      // ROPE: positions [M]
     const float2* rope;  // ROPE: {cos, sin} table [max_pos][32] of the layer kind
     int max_pos;
+    const void* bias;    // BIAS_F32: [N] dtype
 };
 
 template <typename T> struct MfmaOp;
@@ -336,6 +340,28 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 v.w += a.w;
                 *dst = v;
             }
+        } else if constexpr (EPI == EPI_GELU_F32 || EPI == EPI_BIAS_F32) {
+            constexpr int CH = BN / 4;
+            float* C = (float*)p.C;
+            for (int idx = tid; idx < EROWS * CH; idx += NT) {
+                const int sr = idx / CH, c = idx % CH, row = tile_row(sr);
+                if (row >= M) continue;
+                float4 v = *reinterpret_cast<const float4*>(Cs + sr * CP + 4 * c);
+                const int col = bn * BN + 4 * c;
+                if constexpr (EPI == EPI_GELU_F32) {
+                    v.x = gelu_erf(v.x);
+                    v.y = gelu_erf(v.y);
+                    v.z = gelu_erf(v.z);
+                    v.w = gelu_erf(v.w);
+                } else {
+                    const float4 b = Vec4<T>::load((const T*)p.bias + col);
+                    v.x += b.x;
+                    v.y += b.y;
+                    v.z += b.z;
+                    v.w += b.w;
+                }
+                *reinterpret_cast<float4*>(C + (size_t)row * p.N + col) = v;
+            }
         } else {  // EPI_GEGLU
             constexpr int HALF = BN / 2, CH = HALF / 8;
             T* C = (T*)p.C;
@@ -384,6 +410,16 @@ int run_gemm(const GemmArgs& a, hipStream_t s) {
         return launch_tiles<T, 256, 256, 2, 4, EPI, 1>(a, s);
     if (t128 >= MB_GEMM_SMALL_MAX_TILES) return launch_tiles<T, 128, 128, 2, 2, EPI, 2>(a, s);
     if (a.N == D) return launch_tiles<T, 64, 64, 2, 2, EPI, 4>(a, s);
+    return launch_tiles<T, 128, 64, 2, 2, EPI, 3>(a, s);
+}
+
+// fp32 outputs of any width that is a multiple of 64 (the heads: 768, or a vocabulary of
+// 50,368 = 787 x 64 columns).
+template <typename T, int EPI>
+int run_gemm_f32(const GemmArgs& a, hipStream_t s) {
+    if (a.N % 128 == 0) return run_gemm<T, EPI>(a, s);
+    if ((a.K * (int)sizeof(T)) % (128 * kPrefetch) != 0) return MBERT_EUNSUPPORTED;
+    if (a.M <= 512) return launch_tiles<T, 64, 64, 2, 2, EPI, 4>(a, s);
     return launch_tiles<T, 128, 64, 2, 2, EPI, 3>(a, s);
 }
 
@@ -460,4 +496,31 @@ int launch_geglu(mbert_dtype dt, const void* h, int total, const int32_t* meta, 
     }
 }
 
+}  // namespace mbh
+
+namespace mbh {
+int launch_linear_f32(mbert_dtype dt, const void* a_, int M, const void* W, int N, int K,
+                      int gelu, const void* bias, float* out, hipStream_t s) {
+    mb::GemmArgs a{};
+    a.A = a_;
+    a.B = W;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.C = out;
+    a.bias = bias;
+    if (N % 64 != 0 || K != mb::D || (!gelu && !bias)) return MBERT_EUNSUPPORTED;
+    switch (dt) {
+        case MBERT_F32:
+            return gelu ? mb::run_gemm_f32<float, mb::EPI_GELU_F32>(a, s)
+                        : mb::run_gemm_f32<float, mb::EPI_BIAS_F32>(a, s);
+        case MBERT_BF16:
+            return gelu ? mb::run_gemm_f32<mb::bf16, mb::EPI_GELU_F32>(a, s)
+                        : mb::run_gemm_f32<mb::bf16, mb::EPI_BIAS_F32>(a, s);
+        case MBERT_F16:
+            return gelu ? mb::run_gemm_f32<mb::f16, mb::EPI_GELU_F32>(a, s)
+                        : mb::run_gemm_f32<mb::f16, mb::EPI_BIAS_F32>(a, s);
+        default: return MBERT_EUNSUPPORTED;
+    }
+}
 }  // namespace mbh

@@ -31,6 +31,8 @@ __device__ __forceinline__ void store_row12(T* row, int lane, const float v[12])
 // final norm").
 template <typename TW>
 __device__ __forceinline__ void layernorm12(float v[12], const TW* w, int lane, float eps) {
+    float wv[12];
+    load_row12(w, lane, wv);  // issued before the reductions, so its latency overlaps them
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 12; ++i) s += v[i];
@@ -43,8 +45,6 @@ __device__ __forceinline__ void layernorm12(float v[12], const TW* w, int lane, 
     }
     const float var = wave_sum(q) * (1.0f / D);
     const float rstd = 1.0f / sqrtf(var + eps);
-    float wv[12];
-    load_row12(w, lane, wv);
 #pragma unroll
     for (int i = 0; i < 12; ++i) v[i] = v[i] * rstd * wv[i];
 }
@@ -105,14 +105,22 @@ __global__ __launch_bounds__(64 * FWAVES) void final_ln_kernel(const float* __re
     float acc[12];
 #pragma unroll
     for (int i = 0; i < 12; ++i) acc[i] = 0.f;
-    for (int r = wave; r < tl.y; r += FWAVES) {
-        const long row = tl.x + r;
-        float v[12];
-        load_row12(resid + row * D, lane, v);
-        layernorm12(v, w, lane, eps);
-        store_row12(out + row * D, lane, v);
+    // a wave takes rows wave, wave + 16, ... four at a time: the four loads are in flight
+    // together (a row past the tile re-reads the tile's last row and is dropped)
+    constexpr int RB = 4;
+    for (int r0 = wave; r0 < tl.y; r0 += RB * FWAVES) {
+        float v[RB][12];
 #pragma unroll
-        for (int i = 0; i < 12; ++i) acc[i] += v[i];
+        for (int k = 0; k < RB; ++k)
+            load_row12(resid + (long)(tl.x + min(r0 + FWAVES * k, tl.y - 1)) * D, lane, v[k]);
+#pragma unroll
+        for (int k = 0; k < RB; ++k) {
+            if (r0 + FWAVES * k >= tl.y) break;
+            layernorm12(v[k], w, lane, eps);
+            store_row12(out + (long)(tl.x + r0 + FWAVES * k) * D, lane, v[k]);
+#pragma unroll
+            for (int i = 0; i < 12; ++i) acc[i] += v[k][i];
+        }
     }
     if (partials == nullptr) return;
 #pragma unroll
@@ -133,7 +141,7 @@ __global__ __launch_bounds__(64 * FWAVES) void final_ln_kernel(const float* __re
 // §"Implementing it": normalize(pool(x))). An empty sequence pools to zero.
 __global__ __launch_bounds__(256) void pool_kernel(const int* __restrict__ meta, int total_max,
                                                    int S, const float* __restrict__ partials,
-                                                   float* __restrict__ pooled) {
+                                                   float* __restrict__ pooled, int normalize) {
     __shared__ float red[4];
     const MetaView mv = meta_view(const_cast<int*>(meta), total_max, S);
     const int s = blockIdx.x;
@@ -153,9 +161,71 @@ __global__ __launch_bounds__(256) void pool_kernel(const int* __restrict__ meta,
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sq;
     __syncthreads();
     const float nrm = sqrtf(((red[0] + red[1]) + red[2]) + red[3]);
-    const float inv = 1.0f / fmaxf(nrm, 1e-12f);
+    const float inv = normalize ? 1.0f / fmaxf(nrm, 1e-12f) : 1.0f;
 #pragma unroll
     for (int c = 0; c < 3; ++c) pooled[(long)s * D + threadIdx.x + 256 * c] = m[c] * inv;
+}
+
+// Column sums of one work tile of already-normalised rows (the mean pooling of a finished
+// forward), in the same fixed order as the final-norm kernel's partials.
+__global__ __launch_bounds__(64 * FWAVES) void colsum_kernel(const float* __restrict__ out,
+                                                             const int* __restrict__ meta,
+                                                             int total_max, int S,
+                                                             float* __restrict__ partials) {
+    __shared__ float red[FWAVES][D];
+    const MetaView mv = meta_view(const_cast<int*>(meta), total_max, S);
+    const int b = blockIdx.x;
+    if (b >= mv.counts[MBERT_META_NTILES]) return;
+    const int4 tl = mv.tiles[b];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float acc[12];
+#pragma unroll
+    for (int i = 0; i < 12; ++i) acc[i] = 0.f;
+    for (int r = wave; r < tl.y; r += FWAVES) {
+        float v[12];
+        load_row12(out + (long)(tl.x + r) * D, lane, v);
+#pragma unroll
+        for (int i = 0; i < 12; ++i) acc[i] += v[i];
+    }
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[wave][4 * (lane + 64 * c) + e] = acc[4 * c + e];
+    __syncthreads();
+    for (int col = threadIdx.x; col < D; col += 64 * FWAVES) {
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < FWAVES; ++q) sum += red[q][col];
+        partials[(long)b * D + col] = sum;
+    }
+}
+
+// CLS pooling: the first row of each sequence (candding, "ModernBERT", §"Pooling and
+// normalization": index 0), optionally divided by max(L2 norm, 1e-12); an empty sequence
+// pools to zero. One wave per sequence.
+__global__ __launch_bounds__(256) void cls_kernel(const float* __restrict__ out,
+                                                  const int* __restrict__ meta, int total_max,
+                                                  int S, float* __restrict__ pooled,
+                                                  int normalize) {
+    const MetaView mv = meta_view(const_cast<int*>(meta), total_max, S);
+    const int s = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (s >= S) return;
+    const int t0 = mv.seq_tile0[s], t1 = mv.seq_tile0[s + 1];
+    float v[12];
+    if (t1 > t0) {
+        load_row12(out + (long)mv.tiles[t0].z * D, lane, v);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 12; ++i) v[i] = 0.f;
+    }
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) sq += v[i] * v[i];
+    sq = wave_sum(sq);
+    const float inv = normalize ? 1.0f / fmaxf(sqrtf(sq), 1e-12f) : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) v[i] *= inv;
+    store_row12(pooled + (long)s * D, lane, v);
 }
 
 // Standalone rotate-half RoPE on the query and key columns of one qkv row per workgroup
@@ -257,7 +327,7 @@ int launch_final_ln_pool(const float* resid, int total, const int32_t* meta, int
         MB_CHECK_LAUNCH();
     }
     if (pooled && n_seqs > 0) {
-        pool_kernel<<<n_seqs, 256, 0, s>>>(meta, total, n_seqs, partials, pooled);
+        pool_kernel<<<n_seqs, 256, 0, s>>>(meta, total, n_seqs, partials, pooled, 1);
         MB_CHECK_LAUNCH();
     }
     return MBERT_OK;
@@ -284,4 +354,27 @@ int launch_rope(mbert_dtype dt, void* qkv, int total, const int32_t* meta, const
     return MBERT_OK;
 }
 
+}  // namespace mbh
+
+namespace mbh {
+using namespace mb;
+
+int launch_pool(const float* out, int total, const int32_t* meta, int n_seqs, int mode,
+                float* pooled, float* partials, hipStream_t s) {
+    if (n_seqs == 0) return MBERT_OK;
+    const int normalize = (mode & MBERT_POOL_L2) != 0;
+    if ((mode & 1) == MBERT_POOL_CLS) {
+        cls_kernel<<<(n_seqs + 3) / 4, 256, 0, s>>>(out, meta, total, n_seqs, pooled, normalize);
+        MB_CHECK_LAUNCH();
+        return MBERT_OK;
+    }
+    const size_t tmax = tiles_max_for(total, n_seqs);
+    if (tmax > 0) {
+        colsum_kernel<<<(unsigned)tmax, 64 * FWAVES, 0, s>>>(out, meta, total, n_seqs, partials);
+        MB_CHECK_LAUNCH();
+    }
+    pool_kernel<<<n_seqs, 256, 0, s>>>(meta, total, n_seqs, partials, pooled, normalize);
+    MB_CHECK_LAUNCH();
+    return MBERT_OK;
+}
 }  // namespace mbh

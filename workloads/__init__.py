@@ -144,6 +144,23 @@ def make_weights(dims: Dims, dtype: str, seed_key: int, std: float = 0.02) -> di
     return w
 
 
+def make_head_weights(dims: Dims, dtype: str, seed_key: int, n_labels: int = 4,
+                      std: float = 0.02) -> dict:
+    """Random-init weights of the heads on top of the encoder (kgptalkie, §"The Masked-LM
+    Head", §"How Do We Put a Classifier on Top?"): the prediction head's dense [D, D] and norm
+    weight [D], the decoder bias [vocab] (the decoder weight is the embedding table), and a
+    classifier [n_labels, D] with bias [n_labels]. Stream 3 of the generator."""
+    g = rng(seed_key, 3)
+    D = dims.hidden
+    return {
+        "dense": round_to(g.standard_normal((D, D)) * std, dtype),
+        "norm": round_to(1.0 + g.standard_normal(D) * std, dtype),
+        "decoder_bias": round_to(g.standard_normal(dims.vocab) * std, dtype),
+        "cls_W": round_to(g.standard_normal((n_labels, D)) * std, dtype),
+        "cls_b": round_to(g.standard_normal(n_labels) * std, dtype),
+    }
+
+
 @lru_cache(maxsize=2)
 def workload_weights(workload_id: int) -> dict:
     wl = WORKLOADS[workload_id]
