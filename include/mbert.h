@@ -209,6 +209,16 @@ int mbert_final_ln_pool(const float* resid, int total, const int32_t* meta, int 
                         mbert_dtype dtype, const void* w, float eps, float* out,
                         float* pooled, float* partials, void* stream);
 
+/* Attention probabilities of one sequence, every head, for inspection (not used by the
+ * forward): probs [12][n_q][n_k] f32, probs[h][i][j] = softmax over allowed keys of
+ * q_i . k_j / 8 for query rows row0 + i (i < n_q) and key rows row0 + j (j < n_k <= n_q) of
+ * qkv [total,2304] (RoPE already applied), positions counted from row0; a local layer
+ * (is_global = 0) allows |i - j| <= half_window (kgptalkie §"How Does Self-Attention
+ * Work?", §"What Are Local and Global Attention?"). Disallowed keys, and all keys of a query
+ * without any, are 0. n_k < n_q is a padded row: its keys are the real tokens. */
+int mbert_attention_probs(mbert_dtype dtype, const void* qkv, int total, int row0, int n_q,
+                          int n_k, int is_global, int half_window, float* probs, void* stream);
+
 /* Pooling of finished rows out [T,768] f32 (after the final LayerNorm), per sequence of the
  * meta buffer: MBERT_POOL_MEAN, the mean of the sequence's rows (kgptalkie §"How Do We Get
  * One Vector per Text?"), or MBERT_POOL_CLS, its first row (candding §"Pooling and
@@ -279,6 +289,18 @@ int mbert_encode(const mbert_weights* w, const int32_t* ids, const int32_t* cu_s
 int mbert_encode_padded(const mbert_weights* w, const int32_t* ids_pad, const int32_t* mask,
                         int B, int Tpad, void* ws, size_t ws_bytes, float* out_pad,
                         float* pooled, void* stream);
+
+/* The padded batch run as is, without unpadding (what a caller without varlen support
+ * computes): every one of the B*Tpad rows goes through the layers, row b's keys are its
+ * first L_b rows (mask rows must be right-padded: ones, then zeros; otherwise
+ * MBERT_STATUS_BAD_MASK is set and the leading run of ones is used), a query with no key in
+ * its window outputs zeros. out_pad [B,Tpad,768] f32 with zeros at the pads; pooled [B,768]
+ * over the real tokens as in mbert_encode. Real rows agree with mbert_encode_padded (the key
+ * padding mask hides pads exactly: rayaq §"Padding and the key padding mask"); it does
+ * B*Tpad/T times the work. Workspace as mbert_encode_padded. */
+int mbert_encode_padded_keymask(const mbert_weights* w, const int32_t* ids_pad,
+                                const int32_t* mask, int B, int Tpad, void* ws, size_t ws_bytes,
+                                float* out_pad, float* pooled, void* stream);
 
 /* ---------------------------------------------------------------- graphs and timing
  * mbert_graph_capture: records mbert_encode (packed) with the given buffers into a HIP graph

@@ -81,6 +81,8 @@ _SIGNATURES = {
     "mbert_final_ln_pool": ([P, I, P, I, I, P, c_float, P, P, P, P], I),
     "mbert_repad": ([P, P, I, I, P, P], I),
     "mbert_pool": ([P, I, P, I, I, P, P, P], I),
+    "mbert_attention_probs": ([I, P, I, I, I, I, I, I, P, P], I),
+    "mbert_encode_padded_keymask": ([POINTER(mbert_weights), P, P, I, I, P, SZ, P, P, P], I),
     "mbert_head_workspace_bytes": ([I, I], SZ),
     "mbert_mlm_head": ([I, P, I, P, I, P, P, c_float, P, P, I, P, SZ, P, P], I),
     "mbert_classifier_head": ([I, P, I, P, P, c_float, P, P, I, P, SZ, P, P], I),
@@ -263,6 +265,12 @@ def mbert_final_ln_pool(resid, total, meta, n_seqs, dtype, w, eps, out, pooled, 
           ptr(out), ptr(pooled), ptr(partials), stream_handle(stream))
 
 
+def mbert_attention_probs(dtype, qkv, total, row0, n_q, n_k, is_global, half_window, probs,
+                          stream=None):
+    _call("mbert_attention_probs", dtype, ptr(qkv), total, row0, n_q, n_k, int(is_global),
+          half_window, ptr(probs), stream_handle(stream))
+
+
 def mbert_pool(out, total, meta, n_seqs, mode, pooled, partials=None, stream=None):
     _call("mbert_pool", ptr(out), total, ptr(meta), n_seqs, mode, ptr(pooled), ptr(partials),
           stream_handle(stream))
@@ -315,6 +323,13 @@ def mbert_encode_padded(weights, ids_pad, mask, B, Tpad, ws, ws_bytes, out_pad, 
                         stream=None, check=True):
     return _call("mbert_encode_padded", ctypes.byref(weights), ptr(ids_pad), ptr(mask), B, Tpad,
                  ptr(ws), ws_bytes, ptr(out_pad), ptr(pooled), stream_handle(stream), check=check)
+
+
+def mbert_encode_padded_keymask(weights, ids_pad, mask, B, Tpad, ws, ws_bytes, out_pad, pooled,
+                                stream=None, check=True):
+    return _call("mbert_encode_padded_keymask", ctypes.byref(weights), ptr(ids_pad), ptr(mask), B,
+                 Tpad, ptr(ws), ws_bytes, ptr(out_pad), ptr(pooled), stream_handle(stream),
+                 check=check)
 
 
 def mbert_graph_capture(weights, ids, cu_seqlens, n_seqs, total, ws, ws_bytes, out, pooled,

@@ -186,6 +186,33 @@ int encode_impl(const mbert_weights* w, const int32_t* ids, const int32_t* cu, i
     return MBERT_OK;
 }
 
+// The padded batch run as is, every row at its full width (the non-unpadded path): keys are
+// each row's real tokens, pad rows are computed and then zeroed, pooling covers real tokens.
+int encode_padded_keymask_impl(const mbert_weights* w, const int32_t* ids_pad,
+                               const int32_t* mask, int B, int Tpad, void* ws, size_t ws_bytes,
+                               float* out_pad, float* pooled, hipStream_t s) {
+    MB_TRY(check_weights(w));
+    if (B < 0 || Tpad < 0) return MBERT_EINVAL;
+    if ((long)B * (long)Tpad > kMaxRows) return MBERT_ERANGE;
+    if (!ws || !out_pad || !ids_pad || !mask) return MBERT_EINVAL;
+    const int total_max = B * Tpad;
+    const mbert_ws_layout L = make_layout(w->dtype, total_max, B);
+    if (ws_bytes < L.total_bytes) return MBERT_ENOSPC;
+    char* base = static_cast<char*>(ws);
+    int32_t* meta = reinterpret_cast<int32_t*>(base + L.meta);
+    float* resid = reinterpret_cast<float*>(base + L.resid);
+    MB_TRY(mbh::launch_padded_meta(mask, B, Tpad, w->cfg.max_positions, meta, s));
+    if (total_max > 0) {
+        MB_TRY(mbh::launch_embed_ln(w->dtype, ids_pad, total_max, meta, w->tok_emb, w->cfg.vocab,
+                                    w->emb_norm, w->cfg.norm_eps, resid, base + L.h, s));
+        for (int l = 0; l < w->cfg.n_layers; ++l)
+            MB_TRY(run_layer(w, l, total_max, B, base, L, s, nullptr));
+    }
+    return mbh::launch_final_ln_pool(resid, total_max, meta, B, w->dtype, w->final_norm,
+                                     w->cfg.norm_eps, out_pad, pooled,
+                                     reinterpret_cast<float*>(base + L.partials), s);
+}
+
 int encode_padded_impl(const mbert_weights* w, const int32_t* ids_pad, const int32_t* mask, int B,
                        int Tpad, void* ws, size_t ws_bytes, float* out_pad, float* pooled,
                        hipStream_t s, Recorder* rec) {
@@ -391,6 +418,25 @@ int mbert_final_ln_pool(const float* resid, int total, const int32_t* meta, int 
     if (!meta || !w || (total > 0 && (!resid || !out)) || (pooled && !partials)) return MBERT_EINVAL;
     return mbh::launch_final_ln_pool(resid, total, meta, n_seqs, dt, w, eps, out, pooled, partials,
                                      as_stream(stream));
+}
+
+int mbert_encode_padded_keymask(const mbert_weights* w, const int32_t* ids_pad,
+                                const int32_t* mask, int B, int Tpad, void* ws, size_t ws_bytes,
+                                float* out_pad, float* pooled, void* stream) {
+    return encode_padded_keymask_impl(w, ids_pad, mask, B, Tpad, ws, ws_bytes, out_pad, pooled,
+                                      as_stream(stream));
+}
+
+int mbert_attention_probs(mbert_dtype dt, const void* qkv, int total, int row0, int n_q, int n_k,
+                          int is_global, int half_window, float* probs, void* stream) {
+    MB_TRY(check_dtype(dt));
+    MB_TRY(check_sizes(total, 0));
+    if (row0 < 0 || n_q < 0 || n_k < 0 || n_k > n_q || (long)row0 + n_q > total || half_window < 0)
+        return MBERT_EINVAL;
+    if (n_q > 65535 * 16) return MBERT_ERANGE;
+    if (n_q > 0 && (!qkv || !probs)) return MBERT_EINVAL;
+    return mbh::launch_attention_probs(dt, qkv, row0, n_q, n_k, is_global ? 1 : 0, half_window,
+                                       probs, as_stream(stream));
 }
 
 int mbert_pool(const float* out, int total, const int32_t* meta, int n_seqs, int mode,

@@ -171,6 +171,11 @@ int launch_gather_cast(mbert_dtype dt, const float* x, int total, const int32_t*
                        void* out, hipStream_t s);
 int launch_small_linear(mbert_dtype dt, const void* h, const void* W, const void* b, int S, int C,
                         float* out, hipStream_t s);
+// Meta of a padded batch run at full width: B sequences of Tpad rows, keys cut at L_b.
+int launch_padded_meta(const int32_t* mask, int B, int Tpad, int max_pos, int32_t* meta,
+                       hipStream_t s);
+int launch_attention_probs(mbert_dtype dt, const void* qkv, int row0, int n_q, int n_k,
+                           int is_global, int W, float* probs, hipStream_t s);
 int launch_final_ln_pool(const float* resid, int total, const int32_t* meta, int n_seqs,
                          mbert_dtype dt, const void* w, float eps, float* out, float* pooled,
                          float* partials, hipStream_t s);

@@ -92,6 +92,14 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
     int klo, khi, tmp;
     key_range(q0, s0, s1, is_global, W, klo, tmp);
     key_range(q0 + qn - 1, s0, s1, is_global, W, tmp, khi);
+    if (khi < klo) {
+        // no key for any query of the tile (pad rows of a padded batch run at full width,
+        // beyond the window of every real key): zero outputs, as for fully masked rows
+        for (int idx = threadIdx.x; idx < qn * (HD / 4); idx += blockDim.x)
+            Vec4<T>::store(out + (size_t)(q0 + idx / (HD / 4)) * D + head * HD + 4 * (idx % (HD / 4)),
+                           make_float4(0.f, 0.f, 0.f, 0.f));
+        return;
+    }
     const int nkt = (khi - klo) / 64 + 1;
 
     // this lane's query (loads clamped into the tile) and its band
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
     // ---- normalise and write: lane holds d = 32 db + 8 j + 4 g + i of its query
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (n < qcnt) {
-        const float inv = 1.0f / l_tot;
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;  // a query with no key: zeros
         T* op = out + (size_t)(qw0 + n) * D + head * HD;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
@@ -303,6 +311,63 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
                 Vec4<T>::store(op + 32 * db + 8 * j + 4 * g, v);
             }
     }
+}
+
+// Attention probabilities of one sequence, every head, written out in full (a debugging and
+// inspection path, not the forward's): probs[h][i][j] = softmax over the allowed keys j of
+// q_i . k_j / 8 for query rows row0 + i (i < n_q) and key rows row0 + j (j < n_k), positions
+// counted from row0; a local layer allows |i - j| <= W (kgptalkie, "ModernBERT-base
+// Architecture Teardown", §"How Does Self-Attention Work?", §"What Are Local and Global
+// Attention?"). Keys outside the band, and every key of a query that has none, get 0.
+// One workgroup per (query, head); each thread owns keys j = tid + 256 k of the row, which it
+// keeps in the output row between the max, exponent and normalisation passes.
+template <typename T>
+__global__ __launch_bounds__(256) void attn_probs_kernel(const T* __restrict__ qkv, int row0,
+                                                         int n_q, int n_k, int is_global, int W,
+                                                         float* __restrict__ probs) {
+    __shared__ float qs[HD];
+    __shared__ float red[4];
+    const int i = blockIdx.x, head = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+    if (tid < HD) qs[tid] = to_f(qkv[(size_t)(row0 + i) * QKV + head * HD + tid]);
+    __syncthreads();
+    const int lo = is_global ? 0 : max(0, i - W);
+    const int hi = is_global ? n_k - 1 : min(n_k - 1, i + W);
+    float* row = probs + ((size_t)head * n_q + i) * n_k;
+    float mx = -INFINITY;
+    for (int j = tid; j < n_k; j += 256) {
+        float sc = -INFINITY;
+        if (j >= lo && j <= hi) {
+            const T* kp = qkv + (size_t)(row0 + j) * QKV + D + head * HD;
+            float acc = 0.f;
+#pragma unroll
+            for (int d = 0; d < HD; d += 4) {
+                const float4 k4 = Vec4<T>::load(kp + d);
+                acc += qs[d] * k4.x + qs[d + 1] * k4.y + qs[d + 2] * k4.z + qs[d + 3] * k4.w;
+            }
+            sc = acc * 0.125f;
+        }
+        row[j] = sc;
+        mx = fmaxf(mx, sc);
+    }
+    // block max, then block sum (fixed order over the four waves)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    float sum = 0.f;
+    for (int j = tid; j < n_k; j += 256) {
+        const float p = row[j] == -INFINITY ? 0.f : expf(row[j] - mx);
+        row[j] = p;
+        sum += p;
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) red[tid >> 6] = sum;
+    __syncthreads();
+    sum = ((red[0] + red[1]) + red[2]) + red[3];
+    const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+    for (int j = tid; j < n_k; j += 256) row[j] *= inv;
 }
 
 }  // namespace mb
@@ -336,4 +401,26 @@ int launch_attention(mbert_dtype dt, const void* qkv, int total, const int32_t* 
     return MBERT_OK;
 }
 
+}  // namespace mbh
+
+namespace mbh {
+int launch_attention_probs(mbert_dtype dt, const void* qkv, int row0, int n_q, int n_k,
+                           int is_global, int W, float* probs, hipStream_t s) {
+    if (n_q == 0 || n_k == 0) return MBERT_OK;
+    const dim3 grid((unsigned)n_q, mb::NH);
+    switch (dt) {
+        case MBERT_F32:
+            mb::attn_probs_kernel<float><<<grid, 256, 0, s>>>((const float*)qkv, row0, n_q, n_k, is_global, W, probs);
+            break;
+        case MBERT_BF16:
+            mb::attn_probs_kernel<mb::bf16><<<grid, 256, 0, s>>>((const mb::bf16*)qkv, row0, n_q, n_k, is_global, W, probs);
+            break;
+        case MBERT_F16:
+            mb::attn_probs_kernel<mb::f16><<<grid, 256, 0, s>>>((const mb::f16*)qkv, row0, n_q, n_k, is_global, W, probs);
+            break;
+        default: return MBERT_EUNSUPPORTED;
+    }
+    MB_CHECK_LAUNCH();
+    return MBERT_OK;
+}
 }  // namespace mbh

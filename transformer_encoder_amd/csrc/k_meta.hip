@@ -110,6 +110,54 @@ __global__ __launch_bounds__(1024) void pack_meta_kernel(const int* __restrict__
     }
 }
 
+// Padded batch run at full width (no unpadding): row b of the [B, Tpad] batch is one
+// sequence of Tpad query rows whose keys are its first L_b rows, the real tokens of a
+// right-padded mask (the key padding mask: rayaq, "Encoder-only models", §"Padding and the key
+// padding mask"). Tiles {b*Tpad + 128k, rows, b*Tpad, b*Tpad + L_b}; a mask row that is not
+// ones followed by zeros flags MBERT_STATUS_BAD_MASK and keeps its leading run of ones as keys.
+// One workgroup of 1024 threads, a wave per batch row.
+__global__ __launch_bounds__(1024) void padded_meta_kernel(const int* __restrict__ mask, int B,
+                                                           int Tpad, int max_pos,
+                                                           int* __restrict__ meta) {
+    __shared__ int s_status;
+    const int total_max = B * Tpad;
+    const MetaView mv = meta_view(meta, total_max, B);
+    const int nt = (Tpad + TILE - 1) / TILE;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    if (threadIdx.x == 0) s_status = Tpad > max_pos ? MBERT_STATUS_TOO_LONG : 0;
+    __syncthreads();
+    const bool too_long = s_status != 0;
+    int status = 0;
+    for (int b = wave; b < B; b += nw) {
+        const int* m = mask + (long)b * Tpad;
+        // leading run of ones: the first t with m[t] != 1 (Tpad if none)
+        int first = Tpad, any_after = 0;
+        for (int t = lane; t < Tpad; t += 64)
+            if (m[t] != 1) first = min(first, t);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o, 64));
+        for (int t = first + lane; t < Tpad; t += 64) any_after |= m[t] != 0;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) any_after |= __shfl_xor(any_after, o, 64);
+        if (any_after) status |= MBERT_STATUS_BAD_MASK;
+        const int L = first;
+        for (int k = lane; k < nt; k += 64)
+            mv.tiles[b * nt + k] = make_int4(b * Tpad + TILE * k, min(TILE, Tpad - TILE * k),
+                                             b * Tpad, b * Tpad + L);
+        if (lane == 0) mv.seq_tile0[b] = too_long ? 0 : b * nt;
+    }
+    if (status) atomicOr(&s_status, status);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        mv.seq_tile0[B] = too_long ? 0 : B * nt;
+        mv.counts[MBERT_META_TOTAL] = total_max;
+        mv.counts[MBERT_META_MAXLEN] = too_long ? 0 : Tpad;
+        mv.counts[MBERT_META_NTILES] = too_long ? 0 : B * nt;
+        mv.counts[MBERT_META_STATUS] = s_status;
+        for (int i = 4; i < 8; ++i) mv.counts[i] = 0;
+    }
+}
+
 // Position of each token inside its sequence, one workgroup per tile.
 __global__ __launch_bounds__(TILE) void pos_kernel(int* __restrict__ meta, int total_max, int S) {
     const MetaView mv = meta_view(meta, total_max, S);
@@ -289,6 +337,18 @@ int launch_pack_meta(const int32_t* cu, int n_seqs, int total, int max_pos, int3
     const size_t tmax = tiles_max_for(total, n_seqs);
     if (tmax > 0) {
         pos_kernel<<<(unsigned)tmax, TILE, 0, s>>>(meta, total, n_seqs);
+        MB_CHECK_LAUNCH();
+    }
+    return MBERT_OK;
+}
+
+int launch_padded_meta(const int32_t* mask, int B, int Tpad, int max_pos, int32_t* meta,
+                       hipStream_t s) {
+    padded_meta_kernel<<<1, 1024, 0, s>>>(mask, B, Tpad, max_pos, meta);
+    MB_CHECK_LAUNCH();
+    const size_t tmax = tiles_max_for(B * Tpad, B);
+    if (tmax > 0) {
+        pos_kernel<<<(unsigned)tmax, TILE, 0, s>>>(meta, B * Tpad, B);
         MB_CHECK_LAUNCH();
     }
     return MBERT_OK;

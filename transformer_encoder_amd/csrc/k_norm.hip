@@ -106,8 +106,11 @@ __global__ __launch_bounds__(64 * FWAVES) void final_ln_kernel(const float* __re
 #pragma unroll
     for (int i = 0; i < 12; ++i) acc[i] = 0.f;
     // a wave takes rows wave, wave + 16, ... four at a time: the four loads are in flight
-    // together (a row past the tile re-reads the tile's last row and is dropped)
+    // together (a row past the tile re-reads the tile's last row and is dropped). Rows at or
+    // past the sequence's key end (the pad rows of a padded batch run at full width) are
+    // written as zeros and left out of the pooling sums.
     constexpr int RB = 4;
+    const int real = min(tl.y, tl.w - tl.x);
     for (int r0 = wave; r0 < tl.y; r0 += RB * FWAVES) {
         float v[RB][12];
 #pragma unroll
@@ -115,11 +118,17 @@ __global__ __launch_bounds__(64 * FWAVES) void final_ln_kernel(const float* __re
             load_row12(resid + (long)(tl.x + min(r0 + FWAVES * k, tl.y - 1)) * D, lane, v[k]);
 #pragma unroll
         for (int k = 0; k < RB; ++k) {
-            if (r0 + FWAVES * k >= tl.y) break;
-            layernorm12(v[k], w, lane, eps);
-            store_row12(out + (long)(tl.x + r0 + FWAVES * k) * D, lane, v[k]);
+            const int r = r0 + FWAVES * k;
+            if (r >= tl.y) break;
+            if (r < real) {
+                layernorm12(v[k], w, lane, eps);
 #pragma unroll
-            for (int i = 0; i < 12; ++i) acc[i] += v[k][i];
+                for (int i = 0; i < 12; ++i) acc[i] += v[k][i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 12; ++i) v[k][i] = 0.f;
+            }
+            store_row12(out + (long)(tl.x + r) * D, lane, v[k]);
         }
     }
     if (partials == nullptr) return;

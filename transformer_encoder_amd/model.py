@@ -92,6 +92,17 @@ class DeviceModel:
         B.mbert_encode(self.w, ids, cu_seqlens, S, T, ws, ws.numel(), out, pool, stream)
         return out, pool, ws
 
+    def encode_padded_keymask(self, ids_pad, mask, ws=None, stream=None):
+        """Padded batch run at full width without unpadding (pad keys masked)."""
+        import torch
+        Bn, Tp = ids_pad.shape
+        ws = ws if ws is not None else self.workspace(Bn * Tp, Bn)
+        out = torch.empty((Bn, Tp, 768), dtype=torch.float32, device=self.device)
+        pool = torch.empty((Bn, 768), dtype=torch.float32, device=self.device)
+        B.mbert_encode_padded_keymask(self.w, ids_pad, mask, Bn, Tp, ws, ws.numel(), out, pool,
+                                      stream)
+        return out, pool, ws
+
     def encode_padded(self, ids_pad, mask, ws=None, stream=None):
         """Padded batch: ids_pad, mask [B, Tpad] int32 device tensors."""
         import torch
