@@ -376,6 +376,29 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
+    keymask = None
+    if padded and not args.no_heads:
+        # the same padded batch run at full width with a key padding mask (no unpadding)
+        kws = torch.empty_like(ws)
+        kout = torch.empty_like(out)
+        kpool = torch.empty_like(pooled)
+        kfn = lambda: B.mbert_encode_padded_keymask(m.w, ids_pad, mask, Bn, Tp, kws, kws.numel(),
+                                                    kout, kpool, stream)
+        kfn()
+        stream.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(min(args.steps, 20)):
+            kfn()
+        e1.record(stream)
+        stream.synchronize()
+        kms = e0.elapsed_time(e1) / min(args.steps, 20)
+        real = torch.from_numpy(batch["mask"].astype(bool)).to(dev)
+        keymask = {"eager_ms_per_step": round(kms, 4), "tokens_per_s": round(T / (kms * 1e-3), 1),
+                   "rows_computed": Bn * Tp,
+                   "real_rows_equal_unpadded": bool(torch.equal(kout[real], out[real]))}
+        del kws, kout, kpool
+
     heads = None
     if not args.no_heads:
         # the last eager forward's packed rows: the workspace's out region (padded batch) or
@@ -431,6 +454,8 @@ def main():
                      "avg_launch_ms": round(dom_avg_ms, 5),
                      "work_per_launch": work},
     }
+    if keymask is not None:
+        line["padded_keymask"] = keymask
     if heads is not None:
         line["heads"] = heads
     if not args.no_cpu_baseline:
