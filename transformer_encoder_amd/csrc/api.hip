@@ -100,15 +100,32 @@ struct mbert_graph {
     hipGraphExec_t exec = nullptr;
 };
 
+namespace mb {
+LaunchEvents& launch_events() {
+    static thread_local LaunchEvents ev;
+    return ev;
+}
+}  // namespace mb
+
 namespace {
 
-inline void rec_begin(Recorder* r, int kind, hipStream_t s) {
-    if (r && r->t && r->kind == kind && 2 * r->t->used + 1 < (int)r->t->ev.size())
-        (void)hipEventRecord(r->t->ev[2 * r->t->used], s);
+// Arm the thread's launch events with the next slot of the timer (see MB_LAUNCH); a step that
+// launched nothing records both events back to back.
+inline void rec_begin(Recorder* r, int kind, hipStream_t) {
+    if (r && r->t && r->kind == kind && 2 * r->t->used + 1 < (int)r->t->ev.size()) {
+        mb::LaunchEvents& ev = mb::launch_events();
+        ev.start = r->t->ev[2 * r->t->used];
+        ev.stop = r->t->ev[2 * r->t->used + 1];
+    }
 }
 inline void rec_end(Recorder* r, int kind, hipStream_t s) {
     if (r && r->t && r->kind == kind && 2 * r->t->used + 1 < (int)r->t->ev.size()) {
-        (void)hipEventRecord(r->t->ev[2 * r->t->used + 1], s);
+        mb::LaunchEvents& ev = mb::launch_events();
+        if (ev.start != nullptr) {
+            (void)hipEventRecord(ev.start, s);
+            (void)hipEventRecord(ev.stop, s);
+        }
+        ev = mb::LaunchEvents{};
         r->t->used++;
     }
 }

@@ -1,6 +1,7 @@
 // Shared device-side definitions for the gfx950 ModernBERT-base encoder kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -191,6 +192,31 @@ int launch_geglu(mbert_dtype dt, const void* h, int total, const int32_t* meta, 
 int launch_attention(mbert_dtype dt, const void* qkv, int total, const int32_t* meta, int n_seqs,
                      int is_global, int W, void* o, hipStream_t s);
 }  // namespace mbh
+
+// Per-kernel timing: while a timer slot is armed on this thread (the *_timed entry points),
+// launches carry its start / stop events on the kernel dispatch itself
+// (hipExtLaunchKernelGGL), so the elapsed time is the kernels' own, without the launch gap an
+// event recorded before the launch would add. The first launch takes the start event; every
+// launch takes the stop event, so a step of several kernels is timed from the first to the
+// last.
+namespace mb {
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();
+}  // namespace mb
+
+#define MB_LAUNCH(kernel, grid, block, shmem, stream, ...)                                    \
+    do {                                                                                      \
+        ::mb::LaunchEvents& ev_ = ::mb::launch_events();                                      \
+        if (ev_.stop != nullptr) {                                                            \
+            hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), shmem, stream, ev_.start,  \
+                                  ev_.stop, 0, __VA_ARGS__);                                  \
+            ev_.start = nullptr;                                                              \
+        } else {                                                                              \
+            hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), shmem, stream, __VA_ARGS__);  \
+        }                                                                                     \
+    } while (0)
 
 #define MB_CHECK_LAUNCH()                                   \
     do {                                                    \

@@ -383,15 +383,15 @@ int launch_attention(mbert_dtype dt, const void* qkv, int total, const int32_t* 
     const float scale_log2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
     switch (dt) {
         case MBERT_F32:
-            attn_kernel<float><<<grid, 256, 0, s>>>((const float*)qkv, (float*)o, meta, total, n_seqs,
+            MB_LAUNCH((attn_kernel<float>), grid, 256, 0, s, (const float*)qkv, (float*)o, meta, total, n_seqs,
                                                     tmax, is_global, W, scale_log2);
             break;
         case MBERT_BF16:
-            attn_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)qkv, (bf16*)o, meta, total, n_seqs,
+            MB_LAUNCH((attn_kernel<bf16>), grid, 256, 0, s, (const bf16*)qkv, (bf16*)o, meta, total, n_seqs,
                                                    tmax, is_global, W, scale_log2);
             break;
         case MBERT_F16:
-            attn_kernel<f16><<<grid, 256, 0, s>>>((const f16*)qkv, (f16*)o, meta, total, n_seqs,
+            MB_LAUNCH((attn_kernel<f16>), grid, 256, 0, s, (const f16*)qkv, (f16*)o, meta, total, n_seqs,
                                                   tmax, is_global, W, scale_log2);
             break;
         default:
@@ -410,13 +410,13 @@ int launch_attention_probs(mbert_dtype dt, const void* qkv, int row0, int n_q, i
     const dim3 grid((unsigned)n_q, mb::NH);
     switch (dt) {
         case MBERT_F32:
-            mb::attn_probs_kernel<float><<<grid, 256, 0, s>>>((const float*)qkv, row0, n_q, n_k, is_global, W, probs);
+            MB_LAUNCH((mb::attn_probs_kernel<float>), grid, 256, 0, s, (const float*)qkv, row0, n_q, n_k, is_global, W, probs);
             break;
         case MBERT_BF16:
-            mb::attn_probs_kernel<mb::bf16><<<grid, 256, 0, s>>>((const mb::bf16*)qkv, row0, n_q, n_k, is_global, W, probs);
+            MB_LAUNCH((mb::attn_probs_kernel<mb::bf16>), grid, 256, 0, s, (const mb::bf16*)qkv, row0, n_q, n_k, is_global, W, probs);
             break;
         case MBERT_F16:
-            mb::attn_probs_kernel<mb::f16><<<grid, 256, 0, s>>>((const mb::f16*)qkv, row0, n_q, n_k, is_global, W, probs);
+            MB_LAUNCH((mb::attn_probs_kernel<mb::f16>), grid, 256, 0, s, (const mb::f16*)qkv, row0, n_q, n_k, is_global, W, probs);
             break;
         default: return MBERT_EUNSUPPORTED;
     }

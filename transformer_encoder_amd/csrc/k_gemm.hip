@@ -395,8 +395,7 @@ template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int OCC>
 int launch_tiles(const GemmArgs& a, hipStream_t s) {
     const int n = ((a.M + BM - 1) / BM) * (a.N / BN);
     if (n == 0) return MBERT_OK;
-    gemm_kernel<T, BM, BN, NWM, NWN, EPI, kPrefetch, OCC>
-        <<<xcd_gemm_grid(a.M, BM, a.N, BN), 64 * NWM * NWN, 0, s>>>(a);
+    MB_LAUNCH((gemm_kernel<T, BM, BN, NWM, NWN, EPI, kPrefetch, OCC>), xcd_gemm_grid(a.M, BM, a.N, BN), 64 * NWM * NWN, 0, s, a);
     MB_CHECK_LAUNCH();
     return MBERT_OK;
 }

@@ -54,9 +54,9 @@ int launch_gather_cast(mbert_dtype dt, const float* x, int total, const int32_t*
     if (R == 0) return MBERT_OK;
     const unsigned grid = (unsigned)((R + 3) / 4);
     switch (dt) {
-        case MBERT_F32: gather_cast_kernel<float><<<grid, 256, 0, s>>>(x, total, rows, R, (float*)out); break;
-        case MBERT_BF16: gather_cast_kernel<bf16><<<grid, 256, 0, s>>>(x, total, rows, R, (bf16*)out); break;
-        case MBERT_F16: gather_cast_kernel<f16><<<grid, 256, 0, s>>>(x, total, rows, R, (f16*)out); break;
+        case MBERT_F32: MB_LAUNCH((gather_cast_kernel<float>), grid, 256, 0, s, x, total, rows, R, (float*)out); break;
+        case MBERT_BF16: MB_LAUNCH((gather_cast_kernel<bf16>), grid, 256, 0, s, x, total, rows, R, (bf16*)out); break;
+        case MBERT_F16: MB_LAUNCH((gather_cast_kernel<f16>), grid, 256, 0, s, x, total, rows, R, (f16*)out); break;
         default: return MBERT_EUNSUPPORTED;
     }
     MB_CHECK_LAUNCH();
@@ -69,13 +69,13 @@ int launch_small_linear(mbert_dtype dt, const void* h, const void* W, const void
     const unsigned grid = (unsigned)(((long)S * C + 3) / 4);
     switch (dt) {
         case MBERT_F32:
-            small_linear_kernel<float><<<grid, 256, 0, s>>>((const float*)h, (const float*)W, (const float*)b, S, C, out);
+            MB_LAUNCH((small_linear_kernel<float>), grid, 256, 0, s, (const float*)h, (const float*)W, (const float*)b, S, C, out);
             break;
         case MBERT_BF16:
-            small_linear_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)h, (const bf16*)W, (const bf16*)b, S, C, out);
+            MB_LAUNCH((small_linear_kernel<bf16>), grid, 256, 0, s, (const bf16*)h, (const bf16*)W, (const bf16*)b, S, C, out);
             break;
         case MBERT_F16:
-            small_linear_kernel<f16><<<grid, 256, 0, s>>>((const f16*)h, (const f16*)W, (const f16*)b, S, C, out);
+            MB_LAUNCH((small_linear_kernel<f16>), grid, 256, 0, s, (const f16*)h, (const f16*)W, (const f16*)b, S, C, out);
             break;
         default: return MBERT_EUNSUPPORTED;
     }

@@ -324,7 +324,7 @@ using namespace mb;
 
 int launch_rope_tables(float* table, int max_pos, double theta_g, double theta_l, hipStream_t s) {
     const long n = 2L * max_pos * (HD / 2);
-    rope_table_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(reinterpret_cast<float2*>(table),
+    MB_LAUNCH((rope_table_kernel), (unsigned)((n + 255) / 256), 256, 0, s, reinterpret_cast<float2*>(table),
                                                                   max_pos, theta_g, theta_l);
     MB_CHECK_LAUNCH();
     return MBERT_OK;
@@ -332,11 +332,11 @@ int launch_rope_tables(float* table, int max_pos, double theta_g, double theta_l
 
 int launch_pack_meta(const int32_t* cu, int n_seqs, int total, int max_pos, int32_t* meta,
                      hipStream_t s) {
-    pack_meta_kernel<<<1, 1024, 0, s>>>(cu, n_seqs, total, max_pos, meta, total);
+    MB_LAUNCH((pack_meta_kernel), 1, 1024, 0, s, cu, n_seqs, total, max_pos, meta, total);
     MB_CHECK_LAUNCH();
     const size_t tmax = tiles_max_for(total, n_seqs);
     if (tmax > 0) {
-        pos_kernel<<<(unsigned)tmax, TILE, 0, s>>>(meta, total, n_seqs);
+        MB_LAUNCH((pos_kernel), (unsigned)tmax, TILE, 0, s, meta, total, n_seqs);
         MB_CHECK_LAUNCH();
     }
     return MBERT_OK;
@@ -344,11 +344,11 @@ int launch_pack_meta(const int32_t* cu, int n_seqs, int total, int max_pos, int3
 
 int launch_padded_meta(const int32_t* mask, int B, int Tpad, int max_pos, int32_t* meta,
                        hipStream_t s) {
-    padded_meta_kernel<<<1, 1024, 0, s>>>(mask, B, Tpad, max_pos, meta);
+    MB_LAUNCH((padded_meta_kernel), 1, 1024, 0, s, mask, B, Tpad, max_pos, meta);
     MB_CHECK_LAUNCH();
     const size_t tmax = tiles_max_for(B * Tpad, B);
     if (tmax > 0) {
-        pos_kernel<<<(unsigned)tmax, TILE, 0, s>>>(meta, B * Tpad, B);
+        MB_LAUNCH((pos_kernel), (unsigned)tmax, TILE, 0, s, meta, B * Tpad, B);
         MB_CHECK_LAUNCH();
     }
     return MBERT_OK;
@@ -359,13 +359,13 @@ int launch_unpad(const int32_t* ids_pad, const int32_t* mask, int B, int Tpad, i
                  hipStream_t s) {
     const int total_max = B * Tpad;
     if (B > 0) {
-        unpad_count_kernel<<<B, 256, 0, s>>>(mask, Tpad, cu);
+        MB_LAUNCH((unpad_count_kernel), B, 256, 0, s, mask, Tpad, cu);
         MB_CHECK_LAUNCH();
     }
-    unpad_scan_kernel<<<1, 1024, 0, s>>>(cu, B, max_pos, meta, total_max);
+    MB_LAUNCH((unpad_scan_kernel), 1, 1024, 0, s, cu, B, max_pos, meta, total_max);
     MB_CHECK_LAUNCH();
     if (B > 0) {
-        unpad_compact_kernel<<<B, 256, 0, s>>>(ids_pad, mask, Tpad, cu, ids, indices, rowmap, meta,
+        MB_LAUNCH((unpad_compact_kernel), B, 256, 0, s, ids_pad, mask, Tpad, cu, ids, indices, rowmap, meta,
                                               total_max, B);
         MB_CHECK_LAUNCH();
     }
@@ -376,7 +376,7 @@ int launch_key_ranges(const int32_t* meta, int total_max, int n_seqs, int is_glo
                       int32_t* lo, int32_t* hi, hipStream_t s) {
     const size_t tmax = tiles_max_for(total_max, n_seqs);
     if (tmax == 0) return MBERT_OK;
-    key_range_kernel<<<(unsigned)tmax, TILE, 0, s>>>(meta, total_max, n_seqs, is_global, W, lo, hi);
+    MB_LAUNCH((key_range_kernel), (unsigned)tmax, TILE, 0, s, meta, total_max, n_seqs, is_global, W, lo, hi);
     MB_CHECK_LAUNCH();
     return MBERT_OK;
 }
@@ -385,7 +385,7 @@ int launch_repad(const float* out, const int32_t* rowmap, int B, int Tpad, float
                  hipStream_t s) {
     const long rows = (long)B * Tpad;
     if (rows == 0) return MBERT_OK;
-    repad_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(out, rowmap, rows, out_pad);
+    MB_LAUNCH((repad_kernel), (unsigned)((rows + 3) / 4), 256, 0, s, out, rowmap, rows, out_pad);
     MB_CHECK_LAUNCH();
     return MBERT_OK;
 }

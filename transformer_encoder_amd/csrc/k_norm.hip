@@ -272,15 +272,15 @@ int launch_embed_ln(mbert_dtype dt, const int32_t* ids, int total, const int32_t
     int* counts = const_cast<int*>(meta);
     switch (dt) {
         case MBERT_F32:
-            embed_ln_kernel<float><<<grid, 256, 0, s>>>(ids, total, counts, (const float*)emb, vocab,
+            MB_LAUNCH((embed_ln_kernel<float>), grid, 256, 0, s, ids, total, counts, (const float*)emb, vocab,
                                                         (const float*)w, eps, resid, (float*)h);
             break;
         case MBERT_BF16:
-            embed_ln_kernel<bf16><<<grid, 256, 0, s>>>(ids, total, counts, (const bf16*)emb, vocab,
+            MB_LAUNCH((embed_ln_kernel<bf16>), grid, 256, 0, s, ids, total, counts, (const bf16*)emb, vocab,
                                                        (const bf16*)w, eps, resid, (bf16*)h);
             break;
         case MBERT_F16:
-            embed_ln_kernel<f16><<<grid, 256, 0, s>>>(ids, total, counts, (const f16*)emb, vocab,
+            MB_LAUNCH((embed_ln_kernel<f16>), grid, 256, 0, s, ids, total, counts, (const f16*)emb, vocab,
                                                       (const f16*)w, eps, resid, (f16*)h);
             break;
         default:
@@ -296,13 +296,13 @@ int launch_layernorm(mbert_dtype dt, const float* x, int total, const int32_t* m
     const unsigned grid = (unsigned)((total + 3) / 4);
     switch (dt) {
         case MBERT_F32:
-            layernorm_kernel<float><<<grid, 256, 0, s>>>(x, total, meta, (const float*)w, eps, (float*)y);
+            MB_LAUNCH((layernorm_kernel<float>), grid, 256, 0, s, x, total, meta, (const float*)w, eps, (float*)y);
             break;
         case MBERT_BF16:
-            layernorm_kernel<bf16><<<grid, 256, 0, s>>>(x, total, meta, (const bf16*)w, eps, (bf16*)y);
+            MB_LAUNCH((layernorm_kernel<bf16>), grid, 256, 0, s, x, total, meta, (const bf16*)w, eps, (bf16*)y);
             break;
         case MBERT_F16:
-            layernorm_kernel<f16><<<grid, 256, 0, s>>>(x, total, meta, (const f16*)w, eps, (f16*)y);
+            MB_LAUNCH((layernorm_kernel<f16>), grid, 256, 0, s, x, total, meta, (const f16*)w, eps, (f16*)y);
             break;
         default:
             return MBERT_EUNSUPPORTED;
@@ -319,15 +319,15 @@ int launch_final_ln_pool(const float* resid, int total, const int32_t* meta, int
         float* part = pooled ? partials : nullptr;
         switch (dt) {
             case MBERT_F32:
-                final_ln_kernel<float><<<(unsigned)tmax, 64 * FWAVES, 0, s>>>(resid, meta, total, n_seqs,
+                MB_LAUNCH((final_ln_kernel<float>), (unsigned)tmax, 64 * FWAVES, 0, s, resid, meta, total, n_seqs,
                                                                       (const float*)w, eps, out, part);
                 break;
             case MBERT_BF16:
-                final_ln_kernel<bf16><<<(unsigned)tmax, 64 * FWAVES, 0, s>>>(resid, meta, total, n_seqs,
+                MB_LAUNCH((final_ln_kernel<bf16>), (unsigned)tmax, 64 * FWAVES, 0, s, resid, meta, total, n_seqs,
                                                                      (const bf16*)w, eps, out, part);
                 break;
             case MBERT_F16:
-                final_ln_kernel<f16><<<(unsigned)tmax, 64 * FWAVES, 0, s>>>(resid, meta, total, n_seqs,
+                MB_LAUNCH((final_ln_kernel<f16>), (unsigned)tmax, 64 * FWAVES, 0, s, resid, meta, total, n_seqs,
                                                                     (const f16*)w, eps, out, part);
                 break;
             default:
@@ -336,7 +336,7 @@ int launch_final_ln_pool(const float* resid, int total, const int32_t* meta, int
         MB_CHECK_LAUNCH();
     }
     if (pooled && n_seqs > 0) {
-        pool_kernel<<<n_seqs, 256, 0, s>>>(meta, total, n_seqs, partials, pooled, 1);
+        MB_LAUNCH((pool_kernel), n_seqs, 256, 0, s, meta, total, n_seqs, partials, pooled, 1);
         MB_CHECK_LAUNCH();
     }
     return MBERT_OK;
@@ -348,13 +348,13 @@ int launch_rope(mbert_dtype dt, void* qkv, int total, const int32_t* meta, const
     const float2* tab = reinterpret_cast<const float2*>(rope) + (size_t)table * max_pos * (HD / 2);
     switch (dt) {
         case MBERT_F32:
-            rope_kernel<float><<<total, 256, 0, s>>>((float*)qkv, total, meta, tab, max_pos);
+            MB_LAUNCH((rope_kernel<float>), total, 256, 0, s, (float*)qkv, total, meta, tab, max_pos);
             break;
         case MBERT_BF16:
-            rope_kernel<bf16><<<total, 256, 0, s>>>((bf16*)qkv, total, meta, tab, max_pos);
+            MB_LAUNCH((rope_kernel<bf16>), total, 256, 0, s, (bf16*)qkv, total, meta, tab, max_pos);
             break;
         case MBERT_F16:
-            rope_kernel<f16><<<total, 256, 0, s>>>((f16*)qkv, total, meta, tab, max_pos);
+            MB_LAUNCH((rope_kernel<f16>), total, 256, 0, s, (f16*)qkv, total, meta, tab, max_pos);
             break;
         default:
             return MBERT_EUNSUPPORTED;
@@ -373,16 +373,16 @@ int launch_pool(const float* out, int total, const int32_t* meta, int n_seqs, in
     if (n_seqs == 0) return MBERT_OK;
     const int normalize = (mode & MBERT_POOL_L2) != 0;
     if ((mode & 1) == MBERT_POOL_CLS) {
-        cls_kernel<<<(n_seqs + 3) / 4, 256, 0, s>>>(out, meta, total, n_seqs, pooled, normalize);
+        MB_LAUNCH((cls_kernel), (n_seqs + 3) / 4, 256, 0, s, out, meta, total, n_seqs, pooled, normalize);
         MB_CHECK_LAUNCH();
         return MBERT_OK;
     }
     const size_t tmax = tiles_max_for(total, n_seqs);
     if (tmax > 0) {
-        colsum_kernel<<<(unsigned)tmax, 64 * FWAVES, 0, s>>>(out, meta, total, n_seqs, partials);
+        MB_LAUNCH((colsum_kernel), (unsigned)tmax, 64 * FWAVES, 0, s, out, meta, total, n_seqs, partials);
         MB_CHECK_LAUNCH();
     }
-    pool_kernel<<<n_seqs, 256, 0, s>>>(meta, total, n_seqs, partials, pooled, normalize);
+    MB_LAUNCH((pool_kernel), n_seqs, 256, 0, s, meta, total, n_seqs, partials, pooled, normalize);
     MB_CHECK_LAUNCH();
     return MBERT_OK;
 }
