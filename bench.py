@@ -246,6 +246,43 @@ def measure_heads(B, m, wl, ws, rows_ptr, total_max, T, S, stream, steps):
     return res
 
 
+def measure_concurrency(B, m, padded, args_in, out_like, pooled_like, ws_like, steps, warmup):
+    """Throughput with G independent batches in flight on G streams (one captured forward per
+    stream, each with its own workspace and outputs, launched round-robin): the rate a server
+    sees when requests overlap. Reported beside the single-stream value, never as it."""
+    import torch
+    res = {}
+    for G in (2, 4):
+        streams = [torch.cuda.Stream() for _ in range(G)]
+        graphs, keep = [], []
+        for st in streams:
+            with torch.cuda.stream(st):
+                ws = torch.empty_like(ws_like)
+                o = torch.empty_like(out_like)
+                p = torch.empty_like(pooled_like)
+                keep += [ws, o, p]
+                if padded:
+                    ids_pad, mask, Bn, Tp = args_in
+                    g = B.mbert_graph_capture_padded(m.w, ids_pad, mask, Bn, Tp, ws, ws.numel(), o, p, st)
+                else:
+                    ids, cu, S, T = args_in
+                    g = B.mbert_graph_capture(m.w, ids, cu, S, T, ws, ws.numel(), o, p, st)
+            graphs.append(g)
+        for i in range(warmup * G):
+            B.mbert_graph_launch(graphs[i % G], streams[i % G])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            B.mbert_graph_launch(graphs[i % G], streams[i % G])
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        for g in graphs:
+            B.mbert_graph_destroy(g)
+        res[str(G)] = {"ms_per_step": round(dt * 1e3 / steps, 4), "steps": steps}
+        del keep
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -376,6 +413,14 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
+    concurrency = None
+    if not args.no_heads:
+        cargs = (ids_pad, mask, Bn, Tp) if padded else (ids, cu, S, T)
+        concurrency = measure_concurrency(B, m, padded, cargs, out, pooled, ws, args.steps,
+                                          args.warmup)
+        for v in concurrency.values():
+            v["tokens_per_s"] = round(T / (v["ms_per_step"] * 1e-3), 1)
+
     keymask = None
     if padded and not args.no_heads:
         # the same padded batch run at full width with a key padding mask (no unpadding)
@@ -454,6 +499,8 @@ def main():
                      "avg_launch_ms": round(dom_avg_ms, 5),
                      "work_per_launch": work},
     }
+    if concurrency is not None:
+        line["concurrent_streams"] = concurrency
     if keymask is not None:
         line["padded_keymask"] = keymask
     if heads is not None:

@@ -250,20 +250,24 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
             MB_GLOAD(min(kt + P, nk - 1), u);
             __builtin_amdgcn_sched_barrier(0);  // keep the prefetch at the head of the K-step
             const unsigned char* St = smem + (kt & 1) * (BM + BN) * ROWB;
+            // all operand fragments of the K-step are read first, then the MFMAs run back to
+            // back as the reads land
+            u32x4 af[4][FM], bf[4][FN];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                u32x4 af[FM], bf[FN];
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
-                    af[i] = *(const u32x4*)(St + lds_off(wm * WM + 32 * i + lrow, 2 * s + lk));
+                    af[s][i] = *(const u32x4*)(St + lds_off(wm * WM + 32 * i + lrow, 2 * s + lk));
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    bf[j] = *(const u32x4*)(St + lds_off(BM + wn * WN + 32 * j + lrow, 2 * s + lk));
+                    bf[s][j] = *(const u32x4*)(St + lds_off(BM + wn * WN + 32 * j + lrow, 2 * s + lk));
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) MfmaOp<T>::run(af[i], bf[j], acc[i][j]);
-            }
+                    for (int j = 0; j < FN; ++j) MfmaOp<T>::run(af[s][i], bf[s][j], acc[i][j]);
             MB_SSTORE((u + 1) % P, (kt + 1) & 1);
             __syncthreads();
         }
