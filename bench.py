@@ -283,6 +283,38 @@ def measure_concurrency(B, m, padded, args_in, out_like, pooled_like, ws_like, s
     return res
 
 
+def measure_grouped(B, m, ids_pad, mask, Bn, Tp, out_ref, pooled_ref, steps, warmup):
+    """One batch's forward split into G groups of whole sequences on G streams (one captured
+    graph with a branch per group): time per forward and whether it equals the single-stream
+    forward bit for bit."""
+    import torch
+    res = {}
+    for G in (2, 4, 8):
+        streams = [torch.cuda.Stream() for _ in range(G - 1)]
+        main_s = torch.cuda.Stream()
+        nbytes = B.mbert_workspace_bytes_grouped(m.cfg, m.dtype, Bn, Tp, G)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        o = torch.empty_like(out_ref)
+        p = torch.empty_like(pooled_ref)
+        g = B.mbert_graph_capture_padded_grouped(m.w, ids_pad, mask, Bn, Tp, G, ws, nbytes, o, p,
+                                                 streams, main_s)
+        for _ in range(warmup):
+            B.mbert_graph_launch(g, main_s)
+        main_s.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main_s)
+        for _ in range(steps):
+            B.mbert_graph_launch(g, main_s)
+        e1.record(main_s)
+        main_s.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        B.mbert_graph_destroy(g)
+        res[str(G)] = {"graph_ms_per_step": round(ms, 4),
+                       "equal_to_single_stream": bool(torch.equal(o, out_ref) and torch.equal(p, pooled_ref))}
+        del ws, o, p
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -413,6 +445,12 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
+    grouped = None
+    if padded and not args.no_heads:
+        grouped = measure_grouped(B, m, ids_pad, mask, Bn, Tp, out, pooled, args.steps, args.warmup)
+        for v in grouped.values():
+            v["tokens_per_s"] = round(T / (v["graph_ms_per_step"] * 1e-3), 1)
+
     concurrency = None
     if not args.no_heads:
         cargs = (ids_pad, mask, Bn, Tp) if padded else (ids, cu, S, T)
@@ -499,6 +537,8 @@ def main():
                      "avg_launch_ms": round(dom_avg_ms, 5),
                      "work_per_launch": work},
     }
+    if grouped is not None:
+        line["grouped_streams"] = grouped
     if concurrency is not None:
         line["concurrent_streams"] = concurrency
     if keymask is not None:

@@ -302,6 +302,20 @@ int mbert_encode_padded_keymask(const mbert_weights* w, const int32_t* ids_pad,
                                 const int32_t* mask, int B, int Tpad, void* ws, size_t ws_bytes,
                                 float* out_pad, float* pooled, void* stream);
 
+/* The padded batch split into n_groups groups of consecutive rows (whole sequences; the last
+ * group may hold fewer), each group's forward (as mbert_encode_padded) enqueued on its own
+ * stream: group 0 on `stream`, group g on streams[g-1] (n_groups-1 distinct streams, none of
+ * them `stream`), forked from `stream` and joined back into it with events, so the call is
+ * ordered on `stream` like any other. Sequences never interact, so every output is the
+ * same as mbert_encode_padded's; the groups' kernels overlap on the GPU. The workspace holds
+ * one region per group: mbert_workspace_bytes_grouped() bytes. n_groups is clamped to B. */
+size_t mbert_workspace_bytes_grouped(const mbert_config* cfg, mbert_dtype dtype, int B, int Tpad,
+                                     int n_groups);
+int mbert_encode_padded_grouped(const mbert_weights* w, const int32_t* ids_pad,
+                                const int32_t* mask, int B, int Tpad, int n_groups, void* ws,
+                                size_t ws_bytes, float* out_pad, float* pooled,
+                                void* const* streams, void* stream);
+
 /* ---------------------------------------------------------------- graphs and timing
  * mbert_graph_capture: records mbert_encode (packed) with the given buffers into a HIP graph
  * on `stream` and instantiates it; mbert_graph_launch replays it on `stream`. The buffers
@@ -313,6 +327,12 @@ int mbert_graph_capture(const mbert_weights* w, const int32_t* ids, const int32_
 int mbert_graph_capture_padded(const mbert_weights* w, const int32_t* ids_pad,
                                const int32_t* mask, int B, int Tpad, void* ws, size_t ws_bytes,
                                float* out_pad, float* pooled, void* stream, mbert_graph** graph);
+/* As mbert_graph_capture_padded for mbert_encode_padded_grouped: the captured graph has one
+ * branch per group. */
+int mbert_graph_capture_padded_grouped(const mbert_weights* w, const int32_t* ids_pad,
+                                       const int32_t* mask, int B, int Tpad, int n_groups,
+                                       void* ws, size_t ws_bytes, float* out_pad, float* pooled,
+                                       void* const* streams, void* stream, mbert_graph** graph);
 int mbert_graph_launch(mbert_graph* graph, void* stream);
 int mbert_graph_destroy(mbert_graph* graph);
 

@@ -133,6 +133,21 @@ def test_encode_validation_paths(lib):
     assert lib.mbert_encode_padded(ctypes.byref(w), fake, fake, 8, 512, fake, need_p - 1, fake,
                                    None, None) == B.MBERT_ENOSPC
     assert lib.mbert_layer(ctypes.byref(w), 2, 300, 1, fake, need, None) == B.MBERT_EINVAL
+    # grouped padded forward: workspace per group, distinct extra streams
+    one = B.mbert_workspace_bytes(w.cfg, B.MBERT_BF16, 4 * 512, 4)
+    assert B.mbert_workspace_bytes_grouped(w.cfg, B.MBERT_BF16, 8, 512, 2) == 2 * one
+    assert B.mbert_workspace_bytes_grouped(w.cfg, B.MBERT_BF16, 8, 512, 1) == need_p
+    assert B.mbert_workspace_bytes_grouped(w.cfg, B.MBERT_BF16, 8, 512, 0) == 0
+    grp = lib.mbert_encode_padded_grouped
+    s_main = ctypes.c_void_p(0x9000)
+    same = (ctypes.c_void_p * 1)(0x9000)
+    other = (ctypes.c_void_p * 1)(0xA000)
+    assert grp(ctypes.byref(w), fake, fake, 8, 512, 2, fake, 2 * one, fake, None, same,
+               s_main) == B.MBERT_EINVAL
+    assert grp(ctypes.byref(w), fake, fake, 8, 512, 2, fake, 2 * one - 1, fake, None, other,
+               s_main) == B.MBERT_ENOSPC
+    assert grp(ctypes.byref(w), fake, fake, 8, 512, 0, fake, 2 * one, fake, None, other,
+               s_main) == B.MBERT_EINVAL
 
 
 def test_step_validation_paths(lib):

@@ -94,6 +94,11 @@ _SIGNATURES = {
     "mbert_graph_capture": ([POINTER(mbert_weights), P, P, I, I, P, SZ, P, P, P, POINTER(P)], I),
     "mbert_graph_capture_padded": ([POINTER(mbert_weights), P, P, I, I, P, SZ, P, P, P,
                                     POINTER(P)], I),
+    "mbert_workspace_bytes_grouped": ([POINTER(mbert_config), I, I, I, I], SZ),
+    "mbert_encode_padded_grouped": ([POINTER(mbert_weights), P, P, I, I, I, P, SZ, P, P, POINTER(P),
+                                     P], I),
+    "mbert_graph_capture_padded_grouped": ([POINTER(mbert_weights), P, P, I, I, I, P, SZ, P, P,
+                                            POINTER(P), P, POINTER(P)], I),
     "mbert_graph_launch": ([P, P], I),
     "mbert_graph_destroy": ([P], I),
     "mbert_timer_create": ([I, POINTER(P)], I),
@@ -345,6 +350,31 @@ def mbert_graph_capture_padded(weights, ids_pad, mask, B, Tpad, ws, ws_bytes, ou
     g = c_void_p()
     _call("mbert_graph_capture_padded", ctypes.byref(weights), ptr(ids_pad), ptr(mask), B, Tpad,
           ptr(ws), ws_bytes, ptr(out_pad), ptr(pooled), stream_handle(stream), ctypes.byref(g))
+    return g.value
+
+
+def _stream_array(streams):
+    return (c_void_p * max(1, len(streams)))(*[stream_handle(x) for x in streams])
+
+
+def mbert_workspace_bytes_grouped(cfg, dtype, B, Tpad, n_groups) -> int:
+    return lib().mbert_workspace_bytes_grouped(ctypes.byref(cfg), dtype, B, Tpad, n_groups)
+
+
+def mbert_encode_padded_grouped(weights, ids_pad, mask, B, Tpad, n_groups, ws, ws_bytes, out_pad,
+                                pooled, streams, stream=None, check=True):
+    """streams: the n_groups - 1 extra streams (torch.cuda.Stream objects)."""
+    return _call("mbert_encode_padded_grouped", ctypes.byref(weights), ptr(ids_pad), ptr(mask), B,
+                 Tpad, n_groups, ptr(ws), ws_bytes, ptr(out_pad), ptr(pooled),
+                 _stream_array(streams), stream_handle(stream), check=check)
+
+
+def mbert_graph_capture_padded_grouped(weights, ids_pad, mask, B, Tpad, n_groups, ws, ws_bytes,
+                                       out_pad, pooled, streams, stream) -> int:
+    g = c_void_p()
+    _call("mbert_graph_capture_padded_grouped", ctypes.byref(weights), ptr(ids_pad), ptr(mask), B,
+          Tpad, n_groups, ptr(ws), ws_bytes, ptr(out_pad), ptr(pooled), _stream_array(streams),
+          stream_handle(stream), ctypes.byref(g))
     return g.value
 
 

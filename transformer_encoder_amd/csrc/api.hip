@@ -1,6 +1,7 @@
 // The C ABI (include/mbert.h): argument validation, workspace layout, layer sequencing,
 // HIP graph capture and per-kernel timing. Host code only; every step of the forward runs
 // in the kernels of k_meta / k_norm / k_gemm / k_attn.
+#include <algorithm>
 #include <climits>
 #include <new>
 #include <vector>
@@ -264,6 +265,65 @@ int encode_padded_impl(const mbert_weights* w, const int32_t* ids_pad, const int
     MB_TRY(mbh::launch_repad(out, reinterpret_cast<int32_t*>(base + L.rowmap), B, Tpad, out_pad, s));
     return MBERT_OK;
 }
+
+// A padded batch split into groups of consecutive rows (whole sequences), each group's whole
+// forward on its own stream, forked from and joined back into `s` with events. Rows never
+// interact across sequences, so every output row is computed exactly as in one forward; the
+// groups' kernels overlap, which fills the GPU when one batch's kernels are latency-bound.
+struct GroupSplit {
+    int groups, per;  // number of groups, batch rows per group (the last may hold fewer)
+};
+GroupSplit group_split(int B, int n_groups) {
+    GroupSplit g{1, B};
+    if (n_groups <= 1 || B <= 1) return g;
+    g.per = (B + n_groups - 1) / n_groups;
+    g.groups = (B + g.per - 1) / g.per;
+    return g;
+}
+
+int encode_padded_grouped_impl(const mbert_weights* w, const int32_t* ids_pad,
+                               const int32_t* mask, int B, int Tpad, int n_groups, void* ws,
+                               size_t ws_bytes, float* out_pad, float* pooled,
+                               const hipStream_t* extra, hipStream_t s) {
+    MB_TRY(check_weights(w));
+    if (B < 0 || Tpad < 0 || n_groups < 1) return MBERT_EINVAL;
+    if ((long)B * (long)Tpad > kMaxRows) return MBERT_ERANGE;
+    const GroupSplit g = group_split(B, n_groups);
+    if (g.groups == 1)
+        return encode_padded_impl(w, ids_pad, mask, B, Tpad, ws, ws_bytes, out_pad, pooled, s,
+                                  nullptr);
+    if (!ws || !out_pad || !ids_pad || !mask || !extra) return MBERT_EINVAL;
+    for (int i = 0; i < g.groups - 1; ++i)
+        if (extra[i] == nullptr || extra[i] == s) return MBERT_EINVAL;
+    const size_t per_ws = make_layout(w->dtype, g.per * Tpad, g.per).total_bytes;
+    if (ws_bytes < per_ws * (size_t)g.groups) return MBERT_ENOSPC;
+    std::vector<hipEvent_t> ev(g.groups, nullptr);  // ev[0]: fork; ev[i]: join of group i
+    for (auto& e : ev)
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+            for (auto& f : ev)
+                if (f) (void)hipEventDestroy(f);
+            return MBERT_EHIP;
+        }
+    int rc = hipEventRecord(ev[0], s) == hipSuccess ? MBERT_OK : MBERT_EHIP;
+    for (int i = 1; i < g.groups && rc == MBERT_OK; ++i)
+        if (hipStreamWaitEvent(extra[i - 1], ev[0], 0) != hipSuccess) rc = MBERT_EHIP;
+    for (int i = 0; i < g.groups && rc == MBERT_OK; ++i) {
+        const int b0 = i * g.per, nb = std::min(g.per, B - b0);
+        const size_t r0 = (size_t)b0 * Tpad;
+        rc = encode_padded_impl(w, ids_pad + r0, mask + r0, nb, Tpad,
+                                static_cast<char*>(ws) + per_ws * i, per_ws, out_pad + r0 * D,
+                                pooled ? pooled + (size_t)b0 * D : nullptr,
+                                i == 0 ? s : extra[i - 1], nullptr);
+    }
+    // join every forked stream back, also after an error (a capture must end joined)
+    for (int i = 1; i < g.groups; ++i) {
+        (void)hipEventRecord(ev[i], extra[i - 1]);
+        (void)hipStreamWaitEvent(s, ev[i], 0);
+    }
+    for (auto& e : ev) (void)hipEventDestroy(e);
+    return rc;
+}
+
 
 }  // namespace
 
@@ -544,6 +604,14 @@ size_t mbert_workspace_bytes(const mbert_config* c, mbert_dtype dt, int total_ma
     return make_layout(dt, total_max, n_seqs).total_bytes;
 }
 
+size_t mbert_workspace_bytes_grouped(const mbert_config* c, mbert_dtype dt, int B, int Tpad,
+                                     int n_groups) {
+    if (check_cfg(c) || check_dtype(dt) || B < 0 || Tpad < 0 || n_groups < 1) return 0;
+    if ((long)B * (long)Tpad > kMaxRows) return 0;
+    const GroupSplit g = group_split(B, n_groups);
+    return make_layout(dt, g.per * Tpad, g.per).total_bytes * (size_t)g.groups;
+}
+
 int mbert_workspace_layout(const mbert_config* c, mbert_dtype dt, int total_max, int n_seqs,
                            mbert_ws_layout* layout) {
     MB_TRY(check_cfg(c));
@@ -576,6 +644,15 @@ int mbert_encode_padded(const mbert_weights* w, const int32_t* ids_pad, const in
                         void* stream) {
     return encode_padded_impl(w, ids_pad, mask, B, Tpad, ws, ws_bytes, out_pad, pooled,
                               as_stream(stream), nullptr);
+}
+
+int mbert_encode_padded_grouped(const mbert_weights* w, const int32_t* ids_pad,
+                                const int32_t* mask, int B, int Tpad, int n_groups, void* ws,
+                                size_t ws_bytes, float* out_pad, float* pooled,
+                                void* const* streams, void* stream) {
+    return encode_padded_grouped_impl(w, ids_pad, mask, B, Tpad, n_groups, ws, ws_bytes, out_pad,
+                                      pooled, reinterpret_cast<const hipStream_t*>(streams),
+                                      as_stream(stream));
 }
 
 // ---------------------------------------------------------------- graphs
@@ -648,6 +725,32 @@ int mbert_graph_capture_padded(const mbert_weights* w, const int32_t* ids_pad, c
         PaddedCtx* x = static_cast<PaddedCtx*>(p);
         return encode_padded_impl(x->w, x->ids_pad, x->mask, x->B, x->Tpad, x->ws, x->ws_bytes,
                                   x->out_pad, x->pooled, x->s, nullptr);
+    }, &c);
+}
+
+struct GroupedCtx {
+    const mbert_weights* w;
+    const int32_t *ids_pad, *mask;
+    int B, Tpad, n_groups;
+    void* ws;
+    size_t ws_bytes;
+    float *out_pad, *pooled;
+    const hipStream_t* extra;
+    hipStream_t s;
+};
+
+int mbert_graph_capture_padded_grouped(const mbert_weights* w, const int32_t* ids_pad,
+                                       const int32_t* mask, int B, int Tpad, int n_groups,
+                                       void* ws, size_t ws_bytes, float* out_pad, float* pooled,
+                                       void* const* streams, void* stream, mbert_graph** graph) {
+    MB_TRY(check_weights(w));
+    GroupedCtx c{w, ids_pad, mask, B, Tpad, n_groups, ws, ws_bytes, out_pad, pooled,
+                 reinterpret_cast<const hipStream_t*>(streams), as_stream(stream)};
+    return capture_common(as_stream(stream), graph, [](void* p) {
+        GroupedCtx* x = static_cast<GroupedCtx*>(p);
+        return encode_padded_grouped_impl(x->w, x->ids_pad, x->mask, x->B, x->Tpad, x->n_groups,
+                                          x->ws, x->ws_bytes, x->out_pad, x->pooled, x->extra,
+                                          x->s);
     }, &c);
 }
 
