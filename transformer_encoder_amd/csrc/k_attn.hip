@@ -6,7 +6,7 @@
 //
 // Work: one workgroup per (work tile of <= 128 query rows of one sequence, head); 4 wave64s,
 // 32 query rows each. K/V tiles of 64 keys stream through two LDS stages (prefetched into
-// registers one tile ahead). The workgroup walks only the keys its band can reach: the whole
+// registers one tile ahead, with unconditional loads). The workgroup walks only the keys its band can reach: the whole
 // sequence on a global layer, [q0 - W, q0 + qn - 1 + W] on a local one; a wave whose own
 // band misses a key tile skips its MFMAs for it.
 //
@@ -22,6 +22,12 @@
 // row's max grows by more than 2^8.
 // The fp32 variant uses v_mfma_f32_32x32x2_f32 and keeps V in natural layout.
 #include "common.hpp"
+
+// K/V tiles held in registers ahead of the LDS stage. One: a second stage gained 2-3 % on
+// 8192-key global layers and lost as much on short sequences.
+#ifndef MB_ATTN_PREFETCH
+#define MB_ATTN_PREFETCH 1
+#endif
 
 namespace mb {
 
@@ -127,49 +133,50 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
 
     // ---- K/V staging
     constexpr int KCH = F32 ? 4 : 2;  // 16-byte chunks per thread for K (and V for fp32)
-    u32x4 rk[KCH], rv[KCH];
-    auto gload = [&](int it) {
+    constexpr int AP = MB_ATTN_PREFETCH;  // K/V tiles held in registers ahead of the LDS stage
+    u32x4 rk[AP][KCH], rv[AP][KCH];
+    auto gload = [&](int it, int u) {
         const int kb = klo + 64 * it;
         if constexpr (F32) {
 #pragma unroll
             for (int i = 0; i < KCH; ++i) {
                 const int key = min(kb + (tid >> 4) + 16 * i, khi);
                 const T* src = qkv + (size_t)key * QKV + head * HD + (tid & 15) * 4;
-                rk[i] = *(const u32x4*)(src + D);
-                rv[i] = *(const u32x4*)(src + 2 * D);
+                rk[u][i] = *(const u32x4*)(src + D);
+                rv[u][i] = *(const u32x4*)(src + 2 * D);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < KCH; ++i) {
                 const int key = min(kb + (tid >> 3) + 32 * i, khi);
-                rk[i] = *(const u32x4*)(qkv + (size_t)key * QKV + D + head * HD + (tid & 7) * 8);
+                rk[u][i] = *(const u32x4*)(qkv + (size_t)key * QKV + D + head * HD + (tid & 7) * 8);
             }
             const int kp = tid >> 3;  // key pair
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int key = min(kb + 2 * kp + i, khi);
-                rv[i] = *(const u32x4*)(qkv + (size_t)key * QKV + 2 * D + head * HD + (tid & 7) * 8);
+                rv[u][i] = *(const u32x4*)(qkv + (size_t)key * QKV + 2 * D + head * HD + (tid & 7) * 8);
             }
         }
     };
-    auto sstore = [&](int st) {
+    auto sstore = [&](int st, int u) {
         if constexpr (F32) {
 #pragma unroll
             for (int i = 0; i < KCH; ++i) {
                 const int off = ((tid >> 4) + 16 * i) * C::KP + (tid & 15) * 4;
-                *(u32x4*)(&Ks[st][off]) = rk[i];
-                *(u32x4*)(&Vs[st][off]) = rv[i];
+                *(u32x4*)(&Ks[st][off]) = rk[u][i];
+                *(u32x4*)(&Vs[st][off]) = rv[u][i];
             }
         } else {
 #pragma unroll
             for (int i = 0; i < KCH; ++i)
-                *(u32x4*)(&Ks[st][((tid >> 3) + 32 * i) * C::KP + (tid & 7) * 8]) = rk[i];
+                *(u32x4*)(&Ks[st][((tid >> 3) + 32 * i) * C::KP + (tid & 7) * 8]) = rk[u][i];
             // transpose: Vt[d][key]; one dword holds keys (2kp, 2kp+1) of one d
             const int kp = tid >> 3, d0 = (tid & 7) * 8;
             unsigned* vt = reinterpret_cast<unsigned*>(&Vs[st][0]);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const unsigned a = rv[0][m], b = rv[1][m];
+                const unsigned a = rv[u][0][m], b = rv[u][1][m];
                 vt[((d0 + 2 * m) * C::VP) / 2 + kp] = (a & 0xFFFFu) | (b << 16);
                 vt[((d0 + 2 * m + 1) * C::VP) / 2 + kp] = (a >> 16) | (b & 0xFFFF0000u);
             }
@@ -184,11 +191,19 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
     }
     float m_run = -INFINITY, l_run = 0.f;
 
-    gload(0);
-    sstore(0);
+    // Every load is unconditional (a tile past the last re-reads the last one): loads under a
+    // branch leave the wait-count pass unsure of what is in flight. Tile t is held in
+    // register slot t % AP; the loop is unrolled AP times so the slots are static.
+#pragma unroll
+    for (int u = 0; u < AP; ++u) gload(min(u, nkt - 1), u);
+    sstore(0, 0);
     __syncthreads();
-    for (int it = 0; it < nkt; ++it) {
-        if (it + 1 < nkt) gload(it + 1);
+    for (int it0 = 0; it0 < nkt; it0 += AP) {
+#pragma unroll
+    for (int u = 0; u < AP; ++u) {
+        const int it = it0 + u;
+        if (it >= nkt) break;  // uniform over the workgroup
+        gload(min(it + AP, nkt - 1), u);
         const int kb = klo + 64 * it;
         const bool active = qcnt > 0 && kb <= whi && kb + 63 >= wlo;
         if (active) {
@@ -293,8 +308,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
                         }
             }
         }
-        if (it + 1 < nkt) sstore((it + 1) & 1);
+        if (it + 1 < nkt) sstore((it + 1) & 1, (u + 1) % AP);
         __syncthreads();
+    }
     }
 
     // ---- normalise and write: lane holds d = 32 db + 8 j + 4 g + i of its query
