@@ -290,7 +290,12 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
         __syncthreads();
         // staged row sr holds tile row (sr / 32) * WM + 32 * i + sr % 32
         auto tile_row = [&](int sr) { return m0 + (sr >> 5) * WM + 32 * i + (sr & 31); };
-        if constexpr (EPI == EPI_STORE) {
+        // Epilogues that read global memory (positions and the RoPE table, the old residual,
+        // the bias) handle a fixed number of items per thread (unrolled): every load is issued
+        // first, from a row clamped into [0, M) so that it is unconditional, and only the
+        // stores test the row. Under `if (row < M)` the items stay a loop that waits for each
+        // load in turn.
+        if constexpr (EPI == EPI_STORE) {  // no global loads: a plain loop
             constexpr int CH = BN / 8;
             T* C = (T*)p.C;
             for (int idx = tid; idx < EROWS * CH; idx += NT) {
@@ -301,23 +306,39 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 store8<T>(C + (size_t)row * p.N + bn * BN + 8 * c, v);
             }
         } else if constexpr (EPI == EPI_ROPE) {
-            constexpr int NHT = BN / HD;  // heads per tile
+            constexpr int NHT = BN / HD, IT = EROWS * NHT * 4 / NT;  // heads per tile, items
+            static_assert(EROWS * NHT * 4 % NT == 0, "items split evenly");
             T* C = (T*)p.C;
             const int c0 = bn * BN;
             const bool rot = c0 < 2 * D;  // query and key columns; value columns pass through
-            for (int idx = tid; idx < EROWS * NHT * 4; idx += NT) {
+            float4 cs[IT][4];             // {cos, sin} of pairs 2q and 2q+1 of each item
+            if (rot) {
+                int pp[IT];
+#pragma unroll
+                for (int k = 0; k < IT; ++k) {
+                    const int sr = (tid + NT * k) / (4 * NHT);
+                    pp[k] = min(max(p.pos[min(tile_row(sr), M - 1)], 0), p.max_pos - 1);
+                }
+#pragma unroll
+                for (int k = 0; k < IT; ++k) {
+                    const int pc = (tid + NT * k) & 3;
+                    const float4* t = reinterpret_cast<const float4*>(p.rope + (size_t)pp[k] * (HD / 2) + 8 * pc);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) cs[k][q] = t[q];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < IT; ++k) {
+                const int idx = tid + NT * k;
                 const int pc = idx & 3, hh = (idx >> 2) % NHT, sr = idx / (4 * NHT), row = tile_row(sr);
-                if (row >= M) continue;
                 float x1[8], x2[8];
                 const float* x = Cs + sr * CP + HD * hh + 8 * pc;
                 load8(x, x1);
                 load8(x + 32, x2);
                 if (rot) {
-                    const int pp = min(max(p.pos[row], 0), p.max_pos - 1);
-                    const float4* cs = reinterpret_cast<const float4*>(p.rope + (size_t)pp * (HD / 2) + 8 * pc);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const float4 t = cs[q];  // {cos, sin} of pairs 2q and 2q+1
+                        const float4 t = cs[k][q];
                         const float a0 = x1[2 * q], b0 = x2[2 * q], a1 = x1[2 * q + 1], b1 = x2[2 * q + 1];
                         x1[2 * q] = a0 * t.x - b0 * t.y;
                         x2[2 * q] = b0 * t.x + a0 * t.y;
@@ -325,48 +346,57 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                         x2[2 * q + 1] = b1 * t.z + a1 * t.w;
                     }
                 }
-                T* dst = C + (size_t)row * QKV + c0 + HD * hh + 8 * pc;
-                store8<T>(dst, x1);
-                store8<T>(dst + 32, x2);
+                if (row < M) {
+                    T* dst = C + (size_t)row * QKV + c0 + HD * hh + 8 * pc;
+                    store8<T>(dst, x1);
+                    store8<T>(dst + 32, x2);
+                }
             }
         } else if constexpr (EPI == EPI_RESID) {
-            constexpr int CH = BN / 4;
+            constexpr int CH = BN / 4, IT = EROWS * CH / NT;
+            static_assert(EROWS * CH % NT == 0, "items split evenly");
             float* R = (float*)p.C;
-            for (int idx = tid; idx < EROWS * CH; idx += NT) {
-                const int sr = idx / CH, c = idx % CH, row = tile_row(sr);
-                if (row >= M) continue;
+            float4 old[IT];
+#pragma unroll
+            for (int k = 0; k < IT; ++k) {
+                const int idx = tid + NT * k, sr = idx / CH, c = idx % CH;
+                old[k] = *reinterpret_cast<const float4*>(R + (size_t)min(tile_row(sr), M - 1) * D + bn * BN + 4 * c);
+            }
+#pragma unroll
+            for (int k = 0; k < IT; ++k) {
+                const int idx = tid + NT * k, sr = idx / CH, c = idx % CH, row = tile_row(sr);
                 const float4 a = *reinterpret_cast<const float4*>(Cs + sr * CP + 4 * c);
-                float4* dst = reinterpret_cast<float4*>(R + (size_t)row * D + bn * BN + 4 * c);
-                float4 v = *dst;
-                v.x += a.x;
-                v.y += a.y;
-                v.z += a.z;
-                v.w += a.w;
-                *dst = v;
+                const float4 v = make_float4(old[k].x + a.x, old[k].y + a.y, old[k].z + a.z, old[k].w + a.w);
+                if (row < M) *reinterpret_cast<float4*>(R + (size_t)row * D + bn * BN + 4 * c) = v;
             }
         } else if constexpr (EPI == EPI_GELU_F32 || EPI == EPI_BIAS_F32) {
-            constexpr int CH = BN / 4;
+            constexpr int CH = BN / 4, IT = EROWS * CH / NT;
+            static_assert(EROWS * CH % NT == 0, "items split evenly");
             float* C = (float*)p.C;
-            for (int idx = tid; idx < EROWS * CH; idx += NT) {
-                const int sr = idx / CH, c = idx % CH, row = tile_row(sr);
-                if (row >= M) continue;
+            float4 b[IT];
+            if constexpr (EPI == EPI_BIAS_F32) {
+#pragma unroll
+                for (int k = 0; k < IT; ++k)
+                    b[k] = Vec4<T>::load((const T*)p.bias + bn * BN + 4 * ((tid + NT * k) % CH));
+            }
+#pragma unroll
+            for (int k = 0; k < IT; ++k) {
+                const int idx = tid + NT * k, sr = idx / CH, c = idx % CH, row = tile_row(sr);
                 float4 v = *reinterpret_cast<const float4*>(Cs + sr * CP + 4 * c);
-                const int col = bn * BN + 4 * c;
                 if constexpr (EPI == EPI_GELU_F32) {
                     v.x = gelu_erf(v.x);
                     v.y = gelu_erf(v.y);
                     v.z = gelu_erf(v.z);
                     v.w = gelu_erf(v.w);
                 } else {
-                    const float4 b = Vec4<T>::load((const T*)p.bias + col);
-                    v.x += b.x;
-                    v.y += b.y;
-                    v.z += b.z;
-                    v.w += b.w;
+                    v.x += b[k].x;
+                    v.y += b[k].y;
+                    v.z += b[k].z;
+                    v.w += b[k].w;
                 }
-                *reinterpret_cast<float4*>(C + (size_t)row * p.N + col) = v;
+                if (row < M) *reinterpret_cast<float4*>(C + (size_t)row * p.N + bn * BN + 4 * c) = v;
             }
-        } else {  // EPI_GEGLU
+        } else {  // EPI_GEGLU (no global loads: a plain loop)
             constexpr int HALF = BN / 2, CH = HALF / 8;
             T* C = (T*)p.C;
             for (int idx = tid; idx < EROWS * CH; idx += NT) {
@@ -376,7 +406,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 load8(Cs + sr * CP + 8 * c, g);
                 load8(Cs + sr * CP + HALF + 8 * c, u);
 #pragma unroll
-                for (int k = 0; k < 8; ++k) g[k] = gelu_erf(g[k]) * u[k];
+                for (int q = 0; q < 8; ++q) g[q] = gelu_erf(g[q]) * u[q];
                 store8<T>(C + (size_t)row * FF + bn * HALF + 8 * c, g);
             }
         }
