@@ -30,6 +30,18 @@
 // real row count read on the device (the padded path sizes its grid for B * Tpad rows).
 #include "common.hpp"
 
+// Operand staging: the number of LDS stages filled straight from global memory, or 0 for the
+// register-staged prefetch. Measured on whole forwards of the padded batch-8 workload (graph
+// replay): register staging everywhere 1.870 ms, two direct stages everywhere 1.914 ms, two for
+// the 2304-wide GEMMs and register staging for the 768-wide ones 1.809 ms, two and three
+// 1.795 ms. (Two direct stages are 5-15 % faster than register staging on the 2304-wide GEMMs
+// alone at 1k-32k rows.)
+#ifndef MB_GEMM_DMA
+#define MB_GEMM_DMA 2
+#endif
+#ifndef MB_GEMM_DMA_N768
+#define MB_GEMM_DMA_N768 3
+#endif
 #ifndef MB_GEMM_BIG_MIN_TILES
 #define MB_GEMM_BIG_MIN_TILES 512
 #endif
@@ -79,6 +91,22 @@ template <> struct MfmaOp<float> {
         c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[3], bv[3], c, 0, 0, 0);
     }
 };
+
+// s_waitcnt immediates (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
+// wait until at most n vector-memory operations are outstanding / until LDS operations drain.
+constexpr unsigned vmcnt_imm(int n) {
+    return (unsigned)(n & 15) | ((unsigned)((n >> 4) & 3) << 14) | (7u << 4) | (15u << 8);
+}
+constexpr unsigned lgkmcnt0_imm() { return 63u | (3u << 14) | (7u << 4); }
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land at lds + 16 i
+// (lds is the same for the whole wave). The builtin exists only for the device target; the
+// host pass, which never runs this, would otherwise drop every kernel that uses it.
+__device__ __forceinline__ void lds_dma16(const unsigned char* g, unsigned char* lds) {
+#if __HIP_DEVICE_COMPILE__
+    __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+#endif
+}
 
 __device__ __forceinline__ float gelu_erf(float z) {
     // z * Phi(z) with the exact error function (candding, §"The feed-forward halves")
@@ -167,8 +195,11 @@ __device__ __forceinline__ void load8(const float* src, float* v) {
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int P, int OCC>
+template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int P, int OCC, int DS = 0>
 __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
+    // DS > 0: operand tiles go from global memory straight into DS LDS stages
+    // (global_load_lds, 16 bytes per lane), DS - 1 K-steps ahead, with explicit wait counts and
+    // raw barriers; DS == 0: register-staged prefetch P K-steps ahead into two LDS stages.
     constexpr int NT = 64 * NWM * NWN;                    // threads
     constexpr int ROWB = 128;  // bytes of K per row per stage; rows are unpadded (swizzled)
     constexpr int KT = ROWB / (int)sizeof(T);
@@ -177,7 +208,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     constexpr int ACH = BM / RSTEP, BCH = BN / RSTEP;
     constexpr int CP = BN + 8;                            // epilogue staging pitch (floats)
     constexpr int EROWS = NWM * 32;                       // rows staged per epilogue pass
-    constexpr int MAIN_BYTES = 2 * (BM + BN) * ROWB;
+    constexpr int MAIN_BYTES = (DS > 0 ? DS : 2) * (BM + BN) * ROWB;
     constexpr int EPI_BYTES = EROWS * CP * 4;
     constexpr int SMEM = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
     static_assert(EPI != EPI_ROPE || BN % 64 == 0, "RoPE tiles hold whole heads");
@@ -195,6 +226,81 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     const int crow = tid >> 3, cchunk = tid & 7;
     const size_t ld = (size_t)p.K * sizeof(T);
 
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    const int nk = p.K / KT;
+    const int lrow = lane & 31, lk = lane >> 5;  // lk: which 16-byte half of a 32-byte k-step
+    if constexpr (DS > 0) {
+    constexpr int NW = NWM * NWN;
+    constexpr int G = (BM + BN) / 8;      // 8-row groups of a stage, 1 KB each
+    static_assert(G % NW == 0, "groups split over the waves");
+    constexpr int GW = G / NW;            // DMA instructions per wave and K-step
+    constexpr int STAGE = (BM + BN) * ROWB;
+    // Group g covers LDS rows 8g .. 8g+7 (A rows first, then B rows); lane L fills row
+    // 8g + L/8 at physical chunk L%8, which holds logical chunk (L%8) ^ swizzle(row).
+    const unsigned char* gsrc[GW];
+#pragma unroll
+    for (int jg = 0; jg < GW; ++jg) {
+        const int g = wave + NW * jg, lrow8 = 8 * g + (lane >> 3);
+        const int c = (lane & 7) ^ ((lrow8 >> 1) & 7);
+        if (g < BM / 8) {
+            const int gr = min(m0 + lrow8, M - 1);
+            gsrc[jg] = (const unsigned char*)p.A + (size_t)gr * ld + c * 16;
+        } else {
+            const int gr = b_row<EPI, BN>(bn, lrow8 - BM);
+            gsrc[jg] = (const unsigned char*)p.B + (size_t)gr * ld + c * 16;
+        }
+    }
+#define MB_DMA(KT_, ST_)                                                                  \
+    do {                                                                                  \
+        _Pragma("unroll") for (int jg = 0; jg < GW; ++jg)                                 \
+            lds_dma16(gsrc[jg] + (size_t)(KT_) * ROWB,                                    \
+                      smem + (ST_) * STAGE + (wave + NW * jg) * 1024);                    \
+    } while (0)
+#pragma unroll
+    for (int st = 0; st < DS - 1; ++st) MB_DMA(min(st, nk - 1), st);
+    for (int kt = 0; kt < nk; ++kt) {
+        // this wave's DMAs for K-step kt are done once at most GW * (DS - 2) are in flight
+        // (loads complete in order); the barrier then makes every wave's part visible and
+        // frees the stage read in the previous step for the next DMA
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(GW * (DS - 2)));
+        __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        MB_DMA(min(kt + DS - 1, nk - 1), (kt + DS - 1) % DS);
+        const unsigned char* St = smem + (kt % DS) * STAGE;
+        u32x4 af[4][FM], bf[4][FN];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[s][i] = *(const u32x4*)(St + lds_off(wm * WM + 32 * i + lrow, 2 * s + lk));
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bf[s][j] = *(const u32x4*)(St + lds_off(BM + wn * WN + 32 * j + lrow, 2 * s + lk));
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) MfmaOp<T>::run(af[s][i], bf[s][j], acc[i][j]);
+    }
+#undef MB_DMA
+    // the last DMAs (re-reads of the last K-step) land before the epilogue reuses the LDS
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    } else {
     const unsigned char* a_ptr[ACH];
     const unsigned char* b_ptr[BCH];
 #pragma unroll
@@ -209,16 +315,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     }
 
     u32x4 ra[P][ACH], rb[P][BCH];
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    const int nk = p.K / KT;
-    const int lrow = lane & 31, lk = lane >> 5;  // lk: which 16-byte half of a 32-byte k-step
 
 #define MB_GLOAD(KT_, U_)                                                                 \
     do {                                                                                  \
@@ -274,6 +371,8 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     }
 #undef MB_GLOAD
 #undef MB_SSTORE
+    }
+
 
     // ---- epilogue, in FM passes: pass i stages block-row i of every wave (EROWS tile rows)
     //      through LDS. A lane holds column (lane & 31) of each 32x32 block and rows
@@ -425,11 +524,12 @@ constexpr int kPrefetch = MB_GEMM_PREFETCH;
 //   256x256, 8 waves of 128x64  - many rows: twice the MFMA work per wave per K-step
 //   128x128, 4 waves of 64x64   - the default
 //   128x64 / 64x64, 4 waves     - few rows: more, shorter workgroups spread over more CUs
-template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int OCC>
+template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int OCC, int DS = MB_GEMM_DMA>
 int launch_tiles(const GemmArgs& a, hipStream_t s) {
     const int n = ((a.M + BM - 1) / BM) * (a.N / BN);
     if (n == 0) return MBERT_OK;
-    MB_LAUNCH((gemm_kernel<T, BM, BN, NWM, NWN, EPI, kPrefetch, OCC>), xcd_gemm_grid(a.M, BM, a.N, BN), 64 * NWM * NWN, 0, s, a);
+    MB_LAUNCH((gemm_kernel<T, BM, BN, NWM, NWN, EPI, kPrefetch, OCC, DS>),
+              xcd_gemm_grid(a.M, BM, a.N, BN), 64 * NWM * NWN, 0, s, a);
     MB_CHECK_LAUNCH();
     return MBERT_OK;
 }
@@ -440,9 +540,9 @@ int run_gemm(const GemmArgs& a, hipStream_t s) {
     const int t128 = ((a.M + 127) / 128) * (a.N / 128);
     const int t256 = ((a.M + 255) / 256) * (a.N / 256);
     if (a.N % 256 == 0 && t256 >= MB_GEMM_BIG_MIN_TILES)
-        return launch_tiles<T, 256, 256, 2, 4, EPI, 1>(a, s);
+        return launch_tiles<T, 256, 256, 2, 4, EPI, 1, (MB_GEMM_DMA > 2 ? 2 : MB_GEMM_DMA)>(a, s);
     if (t128 >= MB_GEMM_SMALL_MAX_TILES) return launch_tiles<T, 128, 128, 2, 2, EPI, 2>(a, s);
-    if (a.N == D) return launch_tiles<T, 64, 64, 2, 2, EPI, 4>(a, s);
+    if (a.N == D) return launch_tiles<T, 64, 64, 2, 2, EPI, 4, MB_GEMM_DMA_N768>(a, s);
     return launch_tiles<T, 128, 64, 2, 2, EPI, 3>(a, s);
 }
 
