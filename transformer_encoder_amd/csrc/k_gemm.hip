@@ -522,8 +522,9 @@ constexpr int kPrefetch = MB_GEMM_PREFETCH;
 // Tile shapes, by grid size (K is 768 or 1152, so a tile lives for only 12-36 K-steps and a
 // small grid is bound by per-workgroup latency and by how evenly the tiles cover 256 CUs):
 //   256x256, 8 waves of 128x64  - many rows: twice the MFMA work per wave per K-step
-//   128x128, 4 waves of 64x64   - the default
-//   128x64 / 64x64, 4 waves     - few rows: more, shorter workgroups spread over more CUs
+//   128x128, 4 waves of 64x64   - mid-sized grids
+//   64x128 (N = 2304) / 64x64 (N = 768), 4 waves - few rows: more, shorter workgroups spread
+//   over more CUs (64x128 measured 0.7 % faster per forward than 128x64 on 2445 rows)
 template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int OCC, int DS = MB_GEMM_DMA>
 int launch_tiles(const GemmArgs& a, hipStream_t s) {
     const int n = ((a.M + BM - 1) / BM) * (a.N / BN);
@@ -543,7 +544,7 @@ int run_gemm(const GemmArgs& a, hipStream_t s) {
         return launch_tiles<T, 256, 256, 2, 4, EPI, 1, (MB_GEMM_DMA > 2 ? 2 : MB_GEMM_DMA)>(a, s);
     if (t128 >= MB_GEMM_SMALL_MAX_TILES) return launch_tiles<T, 128, 128, 2, 2, EPI, 2>(a, s);
     if (a.N == D) return launch_tiles<T, 64, 64, 2, 2, EPI, 4, MB_GEMM_DMA_N768>(a, s);
-    return launch_tiles<T, 128, 64, 2, 2, EPI, 3>(a, s);
+    return launch_tiles<T, 64, 128, 2, 2, EPI, 3>(a, s);
 }
 
 // fp32 outputs of any width that is a multiple of 64 (the heads: 768, or a vocabulary of
