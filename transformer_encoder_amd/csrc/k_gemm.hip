@@ -1,15 +1,17 @@
 // MFMA GEMM for the encoder's four projections: C[M, N] = A[M, K] . B[N, K]^T, both operands
 // K-contiguous (activations row-major, Linear weights stored [out, in]), fp32 accumulation.
 //
-// Main loop: 256 threads = 4 wave64s in a 2x2 arrangement; each wave owns a (BM/2) x (BN/2)
-// sub-tile made of 32x32 MFMA blocks (v_mfma_f32_32x32x16_{bf16,f16}; fp32 inputs use
-// v_mfma_f32_32x32x2_f32, four per 16-byte operand). K is consumed 128 bytes at a time
-// (64 16-bit or 32 fp32 elements). Global loads run P K-tiles ahead of the MFMAs through
-// register staging (K is only 768 or 1152, so a workgroup's whole life is a dozen K-steps and
-// the load latency has to be covered by loads in flight, not by a long loop), and feed two LDS
-// stages, one barrier per K-step. LDS rows are unpadded and XOR-swizzled by 16-byte chunk (see
-// lds_off), which keeps the 16-byte operand reads conflict-free and a 128x64 tile's two stages
-// at 48 KB, three workgroups per CU.
+// Main loop: 4 (or 8) wave64s in a 2x2 (2x4) arrangement; each wave owns a sub-tile made of
+// 32x32 MFMA blocks (v_mfma_f32_32x32x16_{bf16,f16}; fp32 inputs use v_mfma_f32_32x32x2_f32,
+// four per 16-byte operand). K is consumed 128 bytes at a time (64 16-bit or 32 fp32
+// elements); K is only 768 or 1152, so a workgroup's whole life is a dozen K-steps and the
+// load latency has to be covered by loads in flight, not by a long loop. Operand tiles go
+// from global memory straight into LDS (global_load_lds, 16 bytes per lane), DS - 1 K-steps
+// ahead of the MFMAs, with explicit wait counts and one raw barrier per K-step; a register-
+// staged variant (loads P K-steps ahead into registers, stored to two LDS stages) is kept as a
+// compile-time option. LDS rows are unpadded and XOR-swizzled by 16-byte chunk (see lds_off),
+// which keeps the 16-byte operand reads conflict-free. All fragments of a K-step are read
+// before its MFMAs.
 //
 // Epilogue: the fp32 accumulator tile is staged through LDS (row pitch BN + 8 floats, which
 // keeps the two half-waves of an MFMA block on disjoint banks) and then processed row-major,
@@ -26,6 +28,7 @@
 //   GELU_F32 / BIAS_F32 : C (fp32, row pitch N) = gelu_erf(acc) or acc + bias[col], the dense
 //           layer of the prediction head and the biased decoder / classifier Linear
 //           (kgptalkie, §"The Masked-LM Head")
+// Epilogues that read memory issue all their loads first, from rows clamped into range.
 // Work distribution: tiles are spread over the 8 XCDs in contiguous ranges counted from the
 // real row count read on the device (the padded path sizes its grid for B * Tpad rows).
 #include "common.hpp"
