@@ -45,6 +45,45 @@
 #ifndef MB_GEMM_DMA_N768
 #define MB_GEMM_DMA_N768 3
 #endif
+#ifndef MB_GEMM_BUFLDS
+#define MB_GEMM_BUFLDS 1
+#endif
+#ifndef MB_GEMM_PIPE
+#define MB_GEMM_PIPE 1
+#endif
+#ifndef MB_GEMM_BIG_NWN
+#define MB_GEMM_BIG_NWN 4
+#endif
+#ifndef MB_GEMM_MID_DS
+#define MB_GEMM_MID_DS MB_GEMM_DMA
+#endif
+#ifndef MB_GEMM_MID_OCC
+#define MB_GEMM_MID_OCC 2
+#endif
+#ifndef MB_GEMM_MID_RB
+#define MB_GEMM_MID_RB 128
+#endif
+#ifndef MB_GEMM_SMALL_DS
+#define MB_GEMM_SMALL_DS MB_GEMM_DMA
+#endif
+#ifndef MB_GEMM_SMALL_OCC
+#define MB_GEMM_SMALL_OCC 3
+#endif
+#ifndef MB_GEMM_SMALL_RB
+#define MB_GEMM_SMALL_RB 128
+#endif
+#ifndef MB_GEMM_N768_OCC
+#define MB_GEMM_N768_OCC 4
+#endif
+#ifndef MB_GEMM_N768_RB
+#define MB_GEMM_N768_RB 128
+#endif
+#ifndef MB_GEMM_BIG_DS
+#define MB_GEMM_BIG_DS 2
+#endif
+#ifndef MB_GEMM_BIG_RB
+#define MB_GEMM_BIG_RB 128
+#endif
 #ifndef MB_GEMM_BIG_MIN_TILES
 #define MB_GEMM_BIG_MIN_TILES 512
 #endif
@@ -102,6 +141,15 @@ constexpr unsigned vmcnt_imm(int n) {
 }
 constexpr unsigned lgkmcnt0_imm() { return 63u | (3u << 14) | (7u << 4); }
 
+// Barrier for LDS reuse only: waits for this wave's LDS operations, not for its global stores
+// (__syncthreads would also wait for every store in flight, serialising the epilogue passes).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // 16 bytes per lane from global memory straight into LDS: lane i's bytes land at lds + 16 i
 // (lds is the same for the whole wave). The builtin exists only for the device target; the
 // host pass, which never runs this, would otherwise drop every kernel that uses it.
@@ -111,9 +159,33 @@ __device__ __forceinline__ void lds_dma16(const unsigned char* g, unsigned char*
 #endif
 }
 
+// The same through a buffer load (MUBUF, offset = voff + soff from an SGPR base): wait counts
+// for LDS reads then stay exact per instruction, where a global (FLAT) load into LDS makes the
+// compiler wait for every LDS operation before any use.
+__device__ __forceinline__ void lds_dma16_buf(const void* base, unsigned extent, unsigned voff,
+                                              unsigned soff, unsigned char* lds) {
+#if __HIP_DEVICE_COMPILE__
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, extent, 0x00020000),
+        (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+#endif
+}
+
+// The erf form of GELU, z * Phi(z) with Phi(z) = (1 + erf(z / sqrt 2)) / 2 (candding, §"The
+// feed-forward halves"; not the tanh form). erfc(x), x >= 0, comes from the rational-exponential
+// approximation of Abramowitz & Stegun, Handbook of Mathematical Functions, eq. 7.1.26
+// (|error| <= 1.5e-7): erfc(x) ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
+// t = 1 / (1 + p x). Phi is 1 - erfc/2 for z >= 0 and erfc/2 below, without a branch; the
+// result is within 4.3e-7 of the exact GELU in float32 over all z.
 __device__ __forceinline__ float gelu_erf(float z) {
-    // z * Phi(z) with the exact error function (candding, §"The feed-forward halves")
-    return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+    const float x = fabsf(z) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+    float q = fmaf(t, 1.061405429f, -1.453152027f);
+    q = fmaf(t, q, 1.421413741f);
+    q = fmaf(t, q, -0.284496736f);
+    q = fmaf(t, q, 0.254829592f);
+    q *= t * __builtin_amdgcn_exp2f(-(x * x) * 1.4426950408889634f);
+    return z * (z >= 0.f ? fmaf(-0.5f, q, 1.0f) : 0.5f * q);
 }
 
 // Tiles over the 8 XCDs (each with its own L2): the (row-tile, column-tile) grid is cut into
@@ -163,11 +235,17 @@ inline int xcd_gemm_grid(int M, int BM, int N, int BN) {
     return NXCD * worst;
 }
 
-// LDS position of 16-byte chunk c (0..7) of stage row r: rows are 128 bytes, unpadded, and
-// chunk c is stored at slot c ^ ((r >> 1) & 7). Sixteen consecutive rows read at one logical
-// chunk then cover all 64 banks (rows r and r+1 differ by half the banks, pairs of rows by the
-// slot), and the eight lanes that store one row write it contiguously.
-__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+// LDS position of 16-byte chunk c of stage row r. Rows are RB bytes (128 or 64), unpadded.
+// RB = 128: chunk c (0..7) is stored at slot c ^ ((r >> 1) & 7); rows r and r+1 differ by half
+// of the 256-byte bank window, pairs of rows by the slot. RB = 64: chunk c (0..3) at slot
+// c ^ ((r >> 2) & 3); four consecutive rows fill the window, groups of four differ by the slot.
+// Either way sixteen consecutive rows read at one logical chunk cover all 64 banks, and the
+// lanes that store one row write it contiguously.
+template <int RB = 128>
+__device__ __forceinline__ int lds_off(int r, int c) {
+    if constexpr (RB == 128) return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+    else return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+}
 
 template <int EPI, int BN>
 __device__ __forceinline__ int b_row(int bn, int r) {
@@ -179,15 +257,27 @@ __device__ __forceinline__ int b_row(int bn, int r) {
     }
 }
 
+// 16-byte store through a buffer descriptor (base, extent in bytes): a store at or beyond the
+// extent is dropped by the hardware, so rows past the end need no branch (a branch around a
+// store leaves the compiler unsure how many stores are in flight, and it then waits for all).
+__device__ __forceinline__ void buf_store16(u32x4 v, const void* base, unsigned extent, unsigned off) {
+#if __HIP_DEVICE_COMPILE__
+    __builtin_amdgcn_raw_buffer_store_b128(
+        v, __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, extent, 0x00020000),
+        off, 0, 0);
+#endif
+}
+
+// Eight floats as dtype T to byte offset off of a buffer (16 bytes, or 32 for fp32).
 template <typename T>
-__device__ __forceinline__ void store8(T* dst, const float* v) {
+__device__ __forceinline__ void buf_store8(const void* base, unsigned extent, unsigned off, const float* v) {
     if constexpr (sizeof(T) == 4) {
-        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        buf_store16(__builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]}), base, extent, off);
+        buf_store16(__builtin_bit_cast(u32x4, f32x4{v[4], v[5], v[6], v[7]}), base, extent, off + 16);
     } else {
         typedef T t8 __attribute__((ext_vector_type(8)));
         t8 o = {(T)v[0], (T)v[1], (T)v[2], (T)v[3], (T)v[4], (T)v[5], (T)v[6], (T)v[7]};
-        *reinterpret_cast<t8*>(dst) = o;
+        buf_store16(__builtin_bit_cast(u32x4, o), base, extent, off);
     }
 }
 
@@ -198,13 +288,17 @@ __device__ __forceinline__ void load8(const float* src, float* v) {
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int P, int OCC, int DS = 0>
+template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int P, int OCC, int DS = 0,
+          int RB = 128>
 __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     // DS > 0: operand tiles go from global memory straight into DS LDS stages
     // (global_load_lds, 16 bytes per lane), DS - 1 K-steps ahead, with explicit wait counts and
     // raw barriers; DS == 0: register-staged prefetch P K-steps ahead into two LDS stages.
+    // RB: bytes of K per row and K-step (128, or 64 for more stages in the same LDS).
     constexpr int NT = 64 * NWM * NWN;                    // threads
-    constexpr int ROWB = 128;  // bytes of K per row per stage; rows are unpadded (swizzled)
+    constexpr int ROWB = RB;   // bytes of K per row per stage; rows are unpadded (swizzled)
+    static_assert(RB == 128 || (RB == 64 && DS > 0), "64-byte K-steps need direct staging");
+    constexpr int SUB = ROWB / 32;                        // MFMA k-substeps per K-step
     constexpr int KT = ROWB / (int)sizeof(T);
     constexpr int WM = BM / NWM, WN = BN / NWN, FM = WM / 32, FN = WN / 32;
     constexpr int RSTEP = NT / 8;                         // rows per 16-byte-chunk pass
@@ -223,6 +317,33 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     int bm, bn;
     if (!xcd_tile(blockIdx.x, (M + BM - 1) / BM, nbn, M, p.N, bm, bn)) return;
     const int m0 = bm * BM;
+    const int tid0 = threadIdx.x;
+    // staged epilogue row sr of pass i holds tile row (sr / 32) * WM + 32 * i + sr % 32
+    auto tile_row_of = [&](int i, int sr) { return m0 + (sr >> 5) * (BM / NWM) + 32 * i + (sr & 31); };
+    constexpr int R_NHT = BN / HD > 0 ? BN / HD : 1;
+    constexpr int R_IT = EPI == EPI_ROPE ? (NWM * 32) * R_NHT * 4 / (64 * NWM * NWN) : 1;
+    constexpr int S_CH = BN / 4;
+    constexpr int S_IT = EPI == EPI_RESID ? (NWM * 32) * S_CH / (64 * NWM * NWN) : 1;
+    static_assert(EPI != EPI_ROPE || (NWM * 32) * R_NHT * 4 % (64 * NWM * NWN) == 0, "items split evenly");
+    static_assert(EPI != EPI_RESID || (NWM * 32) * S_CH % (64 * NWM * NWN) == 0, "items split evenly");
+    const bool rot = EPI == EPI_ROPE && bn * BN < 2 * D;  // query and key columns are rotated
+    int rpos[(BM / NWM) / 32][R_IT];
+    float4 rcs[2][R_IT][4];
+    f32x4 rold[2][S_IT];
+    float4 fbias[EPI == EPI_BIAS_F32 ? (NWM * 32) * S_CH / (64 * NWM * NWN) : 1];
+    if constexpr (EPI == EPI_ROPE) {
+#pragma unroll
+        for (int i = 0; i < (BM / NWM) / 32; ++i)
+#pragma unroll
+            for (int k = 0; k < R_IT; ++k) {
+                const int sr = (tid0 + 64 * NWM * NWN * k) / (4 * R_NHT);
+                rpos[i][k] = min(max(p.pos[min(tile_row_of(i, sr), M - 1)], 0), p.max_pos - 1);
+            }
+    } else if constexpr (EPI == EPI_BIAS_F32) {
+#pragma unroll
+        for (int k = 0; k < (int)(sizeof(fbias) / sizeof(fbias[0])); ++k)
+            fbias[k] = Vec4<T>::load((const T*)p.bias + bn * BN + 4 * ((tid0 + 64 * NWM * NWN * k) % S_CH));
+    }
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / NWN, wn = wave % NWN;
@@ -241,18 +362,47 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     const int lrow = lane & 31, lk = lane >> 5;  // lk: which 16-byte half of a 32-byte k-step
     if constexpr (DS > 0) {
     constexpr int NW = NWM * NWN;
-    constexpr int G = (BM + BN) / 8;      // 8-row groups of a stage, 1 KB each
+    constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
+    constexpr int RPG = 64 / CPR;         // rows per 1 KB group (one DMA instruction)
+    constexpr int G = (BM + BN) / RPG;    // groups of a stage
     static_assert(G % NW == 0, "groups split over the waves");
     constexpr int GW = G / NW;            // DMA instructions per wave and K-step
     constexpr int STAGE = (BM + BN) * ROWB;
-    // Group g covers LDS rows 8g .. 8g+7 (A rows first, then B rows); lane L fills row
-    // 8g + L/8 at physical chunk L%8, which holds logical chunk (L%8) ^ swizzle(row).
+    // Group g covers LDS rows RPG*g .. RPG*g + RPG-1 (A rows first, then B rows); lane L fills
+    // row RPG*g + L/CPR at physical chunk L%CPR, which holds the logical chunk that lds_off
+    // places there (the swizzle is its own inverse).
+#if MB_GEMM_BUFLDS
+    // Buffer form: A groups (the first AJ of each wave) read from this tile's first row, B
+    // groups from the weight base; offsets are 32-bit and stay inside each extent (rows are
+    // clamped), the K-step goes into the scalar offset.
+    constexpr int AJ = (BM / RPG) / NW;
+    static_assert((BM / RPG) % NW == 0, "A and B groups split evenly over the waves");
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const unsigned char* abase = (const unsigned char*)p.A + (size_t)m0 * ld;
+    const unsigned aext = (unsigned)min((size_t)(M - m0) * ld, (size_t)0xFFFFFFFFu);
+    const unsigned bext = (unsigned)((size_t)(EPI == EPI_GEGLU ? 2 * FF : p.N) * ld);
+    unsigned voff[GW];
+#pragma unroll
+    for (int jg = 0; jg < GW; ++jg) {
+        const int g = wave + NW * jg, lrow8 = RPG * g + lane / CPR;
+        const int c = (lds_off<ROWB>(lrow8, lane % CPR) - lrow8 * ROWB) >> 4;
+        if (jg < AJ) voff[jg] = (unsigned)((min(m0 + lrow8, M - 1) - m0) * ld + c * 16);
+        else voff[jg] = (unsigned)(b_row<EPI, BN>(bn, lrow8 - BM) * ld + c * 16);
+    }
+#define MB_DMA(KT_, ST_)                                                                  \
+    do {                                                                                  \
+        _Pragma("unroll") for (int jg = 0; jg < GW; ++jg)                                 \
+            lds_dma16_buf(jg < AJ ? (const void*)abase : p.B, jg < AJ ? aext : bext,       \
+                          voff[jg], (unsigned)(KT_) * ROWB,                               \
+                          smem + (ST_) * STAGE + (wu + NW * jg) * 1024);                  \
+    } while (0)
+#else
     const unsigned char* gsrc[GW];
 #pragma unroll
     for (int jg = 0; jg < GW; ++jg) {
-        const int g = wave + NW * jg, lrow8 = 8 * g + (lane >> 3);
-        const int c = (lane & 7) ^ ((lrow8 >> 1) & 7);
-        if (g < BM / 8) {
+        const int g = wave + NW * jg, lrow8 = RPG * g + lane / CPR;
+        const int c = (lds_off<ROWB>(lrow8, lane % CPR) - lrow8 * ROWB) >> 4;
+        if (g < BM / RPG) {
             const int gr = min(m0 + lrow8, M - 1);
             gsrc[jg] = (const unsigned char*)p.A + (size_t)gr * ld + c * 16;
         } else {
@@ -266,6 +416,57 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
             lds_dma16(gsrc[jg] + (size_t)(KT_) * ROWB,                                    \
                       smem + (ST_) * STAGE + (wave + NW * jg) * 1024);                    \
     } while (0)
+#endif
+#if MB_GEMM_PIPE
+#define MB_FRAGS(ST_, S_, B_)                                                              \
+    do {                                                                                  \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i) af[B_][i] =                        \
+            *(const u32x4*)((ST_) + lds_off<ROWB>(wm * WM + 32 * i + lrow, 2 * (S_) + lk)); \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j) bf[B_][j] =                        \
+            *(const u32x4*)((ST_) + lds_off<ROWB>(BM + wn * WN + 32 * j + lrow, 2 * (S_) + lk)); \
+    } while (0)
+    // Software pipeline: the fragments of k-substep s + 1 are read while the MFMAs of
+    // substep s run; the wait and barrier that hand over the next stage sit before the last
+    // substep's MFMAs, so the previous substep's MFMAs are still in the pipe meanwhile.
+#pragma unroll
+    for (int st = 0; st < DS; ++st) MB_DMA(min(st, nk - 1), st);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(GW * (DS - 1)));
+    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());  // also retires scalar loads, so that the
+                                                 // LDS wait counts in the loop are exact
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    static_assert(SUB % 2 == 0, "fragment buffers alternate by substep");
+    u32x4 af[2][FM], bf[2][FN];
+    MB_FRAGS(smem, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const unsigned char* St = smem + (kt % DS) * STAGE;
+#pragma unroll
+        for (int s = 0; s < SUB; ++s) {
+            if (s + 1 < SUB) {
+                MB_FRAGS(St, s + 1, (s + 1) & 1);
+            } else {
+                // every wave has read stage kt once its own reads have landed: after the
+                // barrier the stage takes K-step kt + DS, and stage kt + 1 (whose DMAs this
+                // wave has waited for) is visible to all
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(GW * (DS - 2)));
+                __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                MB_DMA(min(kt + DS, nk - 1), kt % DS);
+                MB_FRAGS(smem + ((kt + 1) % DS) * STAGE, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) MfmaOp<T>::run(af[s & 1][i], bf[s & 1][j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#undef MB_FRAGS
+#else
 #pragma unroll
     for (int st = 0; st < DS - 1; ++st) MB_DMA(min(st, nk - 1), st);
     for (int kt = 0; kt < nk; ++kt) {
@@ -279,23 +480,24 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
         asm volatile("" ::: "memory");
         MB_DMA(min(kt + DS - 1, nk - 1), (kt + DS - 1) % DS);
         const unsigned char* St = smem + (kt % DS) * STAGE;
-        u32x4 af[4][FM], bf[4][FN];
+        u32x4 af[SUB][FM], bf[SUB][FN];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < SUB; ++s) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                af[s][i] = *(const u32x4*)(St + lds_off(wm * WM + 32 * i + lrow, 2 * s + lk));
+                af[s][i] = *(const u32x4*)(St + lds_off<ROWB>(wm * WM + 32 * i + lrow, 2 * s + lk));
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bf[s][j] = *(const u32x4*)(St + lds_off(BM + wn * WN + 32 * j + lrow, 2 * s + lk));
+                bf[s][j] = *(const u32x4*)(St + lds_off<ROWB>(BM + wn * WN + 32 * j + lrow, 2 * s + lk));
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < SUB; ++s)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) MfmaOp<T>::run(af[s][i], bf[s][j], acc[i][j]);
     }
+#endif
 #undef MB_DMA
     // the last DMAs (re-reads of the last K-step) land before the epilogue reuses the LDS
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -380,8 +582,40 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     // ---- epilogue, in FM passes: pass i stages block-row i of every wave (EROWS tile rows)
     //      through LDS. A lane holds column (lane & 31) of each 32x32 block and rows
     //      8 * (e / 4) + 4 * (lane / 32) + (e % 4) for accumulator element e.
+    // The vector-memory counter is shared by loads and stores and retires in order, so a pass
+    // that waited for its own loads after the previous pass's stores would also wait for those
+    // stores: every global load of pass i + 1 (the RoPE table rows, the old residual) is issued
+    // before the stores of pass i, from rows clamped into [0, M), and only the stores test the
+    // row. The RoPE positions are loaded before the main loop.
     float* Cs = reinterpret_cast<float*>(smem);
     const int rq = (lane >> 5) * 4;
+    // output rows m0 .. M-1 as one buffer; offsets are relative to row m0
+    const int cpitch = EPI == EPI_ROPE ? QKV * (int)sizeof(T)
+                     : EPI == EPI_RESID ? D * 4
+                     : EPI == EPI_GEGLU ? FF * (int)sizeof(T)
+                     : EPI == EPI_STORE ? p.N * (int)sizeof(T)
+                     : p.N * 4;
+    const void* cbase = (const unsigned char*)p.C + (size_t)m0 * cpitch;
+    const unsigned cext = (unsigned)min((size_t)(M - m0) * cpitch, (size_t)0xFFFFFFFFu);
+    auto issue_loads = [&](int i) {
+        if constexpr (EPI == EPI_ROPE) {  // value tiles load (and ignore) the table too
+#pragma unroll
+            for (int k = 0; k < R_IT; ++k) {
+                const int pc = (tid + NT * k) & 3;
+                const float4* t = reinterpret_cast<const float4*>(p.rope + (size_t)rpos[i][k] * (HD / 2) + 8 * pc);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) rcs[i & 1][k][q] = t[q];
+            }
+        } else if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+            for (int k = 0; k < S_IT; ++k) {
+                const int idx = tid + NT * k, sr = idx / S_CH, c = idx % S_CH;
+                rold[i & 1][k] = *reinterpret_cast<const f32x4*>(
+                    (const float*)p.C + (size_t)min(tile_row_of(i, sr), M - 1) * D + bn * BN + 4 * c);
+            }
+        }
+    };
+    issue_loads(0);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -389,50 +623,25 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 Cs[(wm * 32 + 8 * (e >> 2) + rq + (e & 3)) * CP + wn * WN + 32 * j + lrow] = acc[i][j][e];
-        __syncthreads();
-        // staged row sr holds tile row (sr / 32) * WM + 32 * i + sr % 32
-        auto tile_row = [&](int sr) { return m0 + (sr >> 5) * WM + 32 * i + (sr & 31); };
-        // Epilogues that read global memory (positions and the RoPE table, the old residual,
-        // the bias) handle a fixed number of items per thread (unrolled): every load is issued
-        // first, from a row clamped into [0, M) so that it is unconditional, and only the
-        // stores test the row. Under `if (row < M)` the items stay a loop that waits for each
-        // load in turn.
-        if constexpr (EPI == EPI_STORE) {  // no global loads: a plain loop
-            constexpr int CH = BN / 8;
-            T* C = (T*)p.C;
-            for (int idx = tid; idx < EROWS * CH; idx += NT) {
-                const int sr = idx / CH, c = idx % CH, row = tile_row(sr);
-                if (row >= M) continue;
-                float v[8];
-                load8(Cs + sr * CP + 8 * c, v);
-                store8<T>(C + (size_t)row * p.N + bn * BN + 8 * c, v);
-            }
-        } else if constexpr (EPI == EPI_ROPE) {
-            constexpr int NHT = BN / HD, IT = EROWS * NHT * 4 / NT;  // heads per tile, items
-            static_assert(EROWS * NHT * 4 % NT == 0, "items split evenly");
-            T* C = (T*)p.C;
-            const int c0 = bn * BN;
-            const bool rot = c0 < 2 * D;  // query and key columns; value columns pass through
-            float4 cs[IT][4];             // {cos, sin} of pairs 2q and 2q+1 of each item
-            if (rot) {
-                int pp[IT];
-#pragma unroll
-                for (int k = 0; k < IT; ++k) {
-                    const int sr = (tid + NT * k) / (4 * NHT);
-                    pp[k] = min(max(p.pos[min(tile_row(sr), M - 1)], 0), p.max_pos - 1);
-                }
-#pragma unroll
-                for (int k = 0; k < IT; ++k) {
-                    const int pc = (tid + NT * k) & 3;
-                    const float4* t = reinterpret_cast<const float4*>(p.rope + (size_t)pp[k] * (HD / 2) + 8 * pc);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) cs[k][q] = t[q];
-                }
-            }
+        lds_barrier();
+        if (i + 1 < FM) issue_loads(i + 1);
+        auto tile_row = [&](int sr) { return tile_row_of(i, sr); };
+        if constexpr (EPI == EPI_STORE) {
+            constexpr int CH = BN / 8, IT = EROWS * CH / NT;
+            static_assert(EROWS * CH % NT == 0, "items split evenly");
 #pragma unroll
             for (int k = 0; k < IT; ++k) {
+                const int idx = tid + NT * k, sr = idx / CH, c = idx % CH, row = tile_row(sr);
+                float v[8];
+                load8(Cs + sr * CP + 8 * c, v);
+                buf_store8<T>(cbase, cext, (unsigned)((row - m0) * cpitch + (bn * BN + 8 * c) * (int)sizeof(T)), v);
+            }
+        } else if constexpr (EPI == EPI_ROPE) {
+            const int c0 = bn * BN;
+#pragma unroll
+            for (int k = 0; k < R_IT; ++k) {
                 const int idx = tid + NT * k;
-                const int pc = idx & 3, hh = (idx >> 2) % NHT, sr = idx / (4 * NHT), row = tile_row(sr);
+                const int pc = idx & 3, hh = (idx >> 2) % R_NHT, sr = idx / (4 * R_NHT), row = tile_row(sr);
                 float x1[8], x2[8];
                 const float* x = Cs + sr * CP + HD * hh + 8 * pc;
                 load8(x, x1);
@@ -440,7 +649,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 if (rot) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const float4 t = cs[k][q];
+                        const float4 t = rcs[i & 1][k][q];
                         const float a0 = x1[2 * q], b0 = x2[2 * q], a1 = x1[2 * q + 1], b1 = x2[2 * q + 1];
                         x1[2 * q] = a0 * t.x - b0 * t.y;
                         x2[2 * q] = b0 * t.x + a0 * t.y;
@@ -448,39 +657,22 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                         x2[2 * q + 1] = b1 * t.z + a1 * t.w;
                     }
                 }
-                if (row < M) {
-                    T* dst = C + (size_t)row * QKV + c0 + HD * hh + 8 * pc;
-                    store8<T>(dst, x1);
-                    store8<T>(dst + 32, x2);
-                }
+                const unsigned off = (unsigned)(((row - m0) * QKV + c0 + HD * hh + 8 * pc) * (int)sizeof(T));
+                buf_store8<T>(cbase, cext, off, x1);
+                buf_store8<T>(cbase, cext, off + 32 * (unsigned)sizeof(T), x2);
             }
         } else if constexpr (EPI == EPI_RESID) {
-            constexpr int CH = BN / 4, IT = EROWS * CH / NT;
-            static_assert(EROWS * CH % NT == 0, "items split evenly");
-            float* R = (float*)p.C;
-            float4 old[IT];
 #pragma unroll
-            for (int k = 0; k < IT; ++k) {
-                const int idx = tid + NT * k, sr = idx / CH, c = idx % CH;
-                old[k] = *reinterpret_cast<const float4*>(R + (size_t)min(tile_row(sr), M - 1) * D + bn * BN + 4 * c);
-            }
-#pragma unroll
-            for (int k = 0; k < IT; ++k) {
-                const int idx = tid + NT * k, sr = idx / CH, c = idx % CH, row = tile_row(sr);
-                const float4 a = *reinterpret_cast<const float4*>(Cs + sr * CP + 4 * c);
-                const float4 v = make_float4(old[k].x + a.x, old[k].y + a.y, old[k].z + a.z, old[k].w + a.w);
-                if (row < M) *reinterpret_cast<float4*>(R + (size_t)row * D + bn * BN + 4 * c) = v;
+            for (int k = 0; k < S_IT; ++k) {
+                const int idx = tid + NT * k, sr = idx / S_CH, c = idx % S_CH, row = tile_row(sr);
+                const f32x4 a = *reinterpret_cast<const f32x4*>(Cs + sr * CP + 4 * c);
+                const f32x4 v = rold[i & 1][k] + a;
+                buf_store16(__builtin_bit_cast(u32x4, v), cbase, cext,
+                            (unsigned)(((row - m0) * D + bn * BN + 4 * c) * 4));
             }
         } else if constexpr (EPI == EPI_GELU_F32 || EPI == EPI_BIAS_F32) {
             constexpr int CH = BN / 4, IT = EROWS * CH / NT;
             static_assert(EROWS * CH % NT == 0, "items split evenly");
-            float* C = (float*)p.C;
-            float4 b[IT];
-            if constexpr (EPI == EPI_BIAS_F32) {
-#pragma unroll
-                for (int k = 0; k < IT; ++k)
-                    b[k] = Vec4<T>::load((const T*)p.bias + bn * BN + 4 * ((tid + NT * k) % CH));
-            }
 #pragma unroll
             for (int k = 0; k < IT; ++k) {
                 const int idx = tid + NT * k, sr = idx / CH, c = idx % CH, row = tile_row(sr);
@@ -491,28 +683,29 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                     v.z = gelu_erf(v.z);
                     v.w = gelu_erf(v.w);
                 } else {
-                    v.x += b[k].x;
-                    v.y += b[k].y;
-                    v.z += b[k].z;
-                    v.w += b[k].w;
+                    v.x += fbias[k].x;
+                    v.y += fbias[k].y;
+                    v.z += fbias[k].z;
+                    v.w += fbias[k].w;
                 }
-                if (row < M) *reinterpret_cast<float4*>(C + (size_t)row * p.N + bn * BN + 4 * c) = v;
+                buf_store16(__builtin_bit_cast(u32x4, v), cbase, cext,
+                            (unsigned)((row - m0) * cpitch + (bn * BN + 4 * c) * 4));
             }
-        } else {  // EPI_GEGLU (no global loads: a plain loop)
-            constexpr int HALF = BN / 2, CH = HALF / 8;
-            T* C = (T*)p.C;
-            for (int idx = tid; idx < EROWS * CH; idx += NT) {
-                const int sr = idx / CH, c = idx % CH, row = tile_row(sr);
-                if (row >= M) continue;
+        } else {  // EPI_GEGLU
+            constexpr int HALF = BN / 2, CH = HALF / 8, IT = EROWS * CH / NT;
+            static_assert(EROWS * CH % NT == 0, "items split evenly");
+#pragma unroll
+            for (int k = 0; k < IT; ++k) {
+                const int idx = tid + NT * k, sr = idx / CH, c = idx % CH, row = tile_row(sr);
                 float g[8], u[8];
                 load8(Cs + sr * CP + 8 * c, g);
                 load8(Cs + sr * CP + HALF + 8 * c, u);
 #pragma unroll
                 for (int q = 0; q < 8; ++q) g[q] = gelu_erf(g[q]) * u[q];
-                store8<T>(C + (size_t)row * FF + bn * HALF + 8 * c, g);
+                buf_store8<T>(cbase, cext, (unsigned)((row - m0) * cpitch + (bn * HALF + 8 * c) * (int)sizeof(T)), g);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -528,11 +721,12 @@ constexpr int kPrefetch = MB_GEMM_PREFETCH;
 //   128x128, 4 waves of 64x64   - mid-sized grids
 //   64x128 (N = 2304) / 64x64 (N = 768), 4 waves - few rows: more, shorter workgroups spread
 //   over more CUs (64x128 measured 0.7 % faster per forward than 128x64 on 2445 rows)
-template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int OCC, int DS = MB_GEMM_DMA>
+template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int OCC, int DS = MB_GEMM_DMA,
+          int RB = 128>
 int launch_tiles(const GemmArgs& a, hipStream_t s) {
     const int n = ((a.M + BM - 1) / BM) * (a.N / BN);
     if (n == 0) return MBERT_OK;
-    MB_LAUNCH((gemm_kernel<T, BM, BN, NWM, NWN, EPI, kPrefetch, OCC, DS>),
+    MB_LAUNCH((gemm_kernel<T, BM, BN, NWM, NWN, EPI, kPrefetch, OCC, DS, RB>),
               xcd_gemm_grid(a.M, BM, a.N, BN), 64 * NWM * NWN, 0, s, a);
     MB_CHECK_LAUNCH();
     return MBERT_OK;
@@ -544,10 +738,12 @@ int run_gemm(const GemmArgs& a, hipStream_t s) {
     const int t128 = ((a.M + 127) / 128) * (a.N / 128);
     const int t256 = ((a.M + 255) / 256) * (a.N / 256);
     if (a.N % 256 == 0 && t256 >= MB_GEMM_BIG_MIN_TILES)
-        return launch_tiles<T, 256, 256, 2, 4, EPI, 1, (MB_GEMM_DMA > 2 ? 2 : MB_GEMM_DMA)>(a, s);
-    if (t128 >= MB_GEMM_SMALL_MAX_TILES) return launch_tiles<T, 128, 128, 2, 2, EPI, 2>(a, s);
-    if (a.N == D) return launch_tiles<T, 64, 64, 2, 2, EPI, 4, MB_GEMM_DMA_N768>(a, s);
-    return launch_tiles<T, 64, 128, 2, 2, EPI, 3>(a, s);
+        return launch_tiles<T, 256, 256, 2, MB_GEMM_BIG_NWN, EPI, 1, MB_GEMM_BIG_DS, MB_GEMM_BIG_RB>(a, s);
+    if (t128 >= MB_GEMM_SMALL_MAX_TILES)
+        return launch_tiles<T, 128, 128, 2, 2, EPI, MB_GEMM_MID_OCC, MB_GEMM_MID_DS, MB_GEMM_MID_RB>(a, s);
+    if (a.N == D)
+        return launch_tiles<T, 64, 64, 2, 2, EPI, MB_GEMM_N768_OCC, MB_GEMM_DMA_N768, MB_GEMM_N768_RB>(a, s);
+    return launch_tiles<T, 64, 128, 2, 2, EPI, MB_GEMM_SMALL_OCC, MB_GEMM_SMALL_DS, MB_GEMM_SMALL_RB>(a, s);
 }
 
 // fp32 outputs of any width that is a multiple of 64 (the heads: 768, or a vocabulary of
