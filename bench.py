@@ -324,6 +324,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of the graph")
     ap.add_argument("--no-heads", action="store_true", help="skip the pooling and head timings")
+    ap.add_argument("--no-fold", action="store_true",
+                    help="run the LayerNorms as separate kernels instead of folding them into the GEMMs")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_<kind>_<workload>.{json,md} from two "
                          "rocprofv3 --pmc runs of this script and exit")
@@ -354,7 +356,7 @@ def main():
     lengths = batch["lengths"]
     T = int(batch["cu_seqlens"][-1])
     S = len(lengths)
-    m = DeviceModel(weights, wl.dtype)
+    m = DeviceModel(weights, wl.dtype, fold=not args.no_fold)
     dev = torch.device("cuda", 0)
     stream = torch.cuda.Stream()
     padded = wl.layout == "padded"
@@ -524,6 +526,7 @@ def main():
         "data": "synthetic (seeded uniform token ids, random-init N(0,0.02) weights)",
         "config": {"workload": wl.name, "description": wl.description, "real_tokens": T,
                    "sequences": S, "padded_to": wl.pad_to, "layers": n_layers,
+                   "layernorms": "folded into the GEMMs" if m.folded is not None else "separate kernels",
                    "timed": "eager launches" if args.eager else "HIP graph replay"},
         "mfma_peak_frac": round(flops / (ms * 1e-3) / 1e12 / peak_mfma, 4),
         "algorithmic_tflop_per_step": round(flops / 1e12, 4),

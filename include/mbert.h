@@ -94,7 +94,28 @@ typedef struct {
     const void* final_norm;            /* device [768]                                 */
     const mbert_layer_weights* layers; /* HOST array [cfg.n_layers]                    */
     const float* rope;                 /* device tables from mbert_build_rope_tables   */
+    const void* folded;                /* device buffer from mbert_fold_norms, or NULL */
 } mbert_weights;
+
+/* ---------------------------------------------------------------- folded LayerNorms
+ * The pre-norm LayerNorms inside the stack (attn_norm of layers >= 1, mlp_norm of every
+ * layer; candding §"The pre-norm layer and the final norm") can be folded into the GEMM that
+ * reads them: LN(x) . W^T = rstd * (x . (W o w)^T - mean * c), c_r = sum_k (W o w)[r][k],
+ * with mean and rstd of each row of x (biased variance, eps inside the square root). The
+ * residual GEMMs then also write each row's statistics per 64-column chunk and the residual
+ * rounded to dtype, and no separate LayerNorm kernel runs between them. Only the rounding
+ * point moves: dtype(x) enters the GEMM instead of dtype(LN(x)); the two agree as long as a
+ * row's mean is not large against its spread. MBERT_F16 is not folded: the raw residual of a
+ * trained model can exceed the fp16 range, while its normalised values cannot.
+ * mbert_fold_norms fills `folded` (mbert_folded_bytes(cfg, dtype) bytes, device) from w's
+ * current weights; setting w->folded to it makes mbert_encode, mbert_encode_padded and
+ * mbert_encode_padded_keymask (and their graph captures) use the folded path; mbert_layer
+ * always runs the separate LayerNorm. Re-run after changing a Wqkv, Wi or norm weight.
+ * Layout per layer l: Wqkv o attn_norm [2304,768] dtype, its c [2304] f32, Wi o mlp_norm
+ * [2304,768] dtype, its c [2304] f32, each 256-byte aligned (layer 0's first two unused).
+ * Returns MBERT_EUNSUPPORTED for MBERT_F16, MBERT_ENOSPC if bytes is too small. */
+size_t mbert_folded_bytes(const mbert_config* cfg, mbert_dtype dtype);
+int mbert_fold_norms(const mbert_weights* w, void* folded, size_t bytes, void* stream);
 
 /* ---------------------------------------------------------------- meta buffer layout
  * One int32 device buffer of mbert_meta_ints(total_max, n_seqs) elements:
@@ -260,9 +281,10 @@ int mbert_repad(const float* out, const int32_t* rowmap, int B, int Tpad, float*
  * Device scratch for one forward; the caller allocates mbert_workspace_bytes() bytes
  * (256-byte aligned). Layout (byte offsets from mbert_workspace_layout): resid f32
  * [Tmax,768], h dtype [Tmax,768] (also the attention output), qkv dtype [Tmax,2304] (also the
- * GeGLU output), meta, pool partials, and for the padded path ids/indices/rowmap/cu. */
+ * GeGLU output), meta, pool partials, for the padded path ids/indices/rowmap/cu/out, and for
+ * folded LayerNorms xs dtype [Tmax,768] (the residual rounded) and rstats f32 [Tmax,12,2]. */
 typedef struct {
-    size_t resid, h, qkv, meta, partials, ids, indices, rowmap, cu, out, total_bytes;
+    size_t resid, h, qkv, meta, partials, ids, indices, rowmap, cu, out, xs, rstats, total_bytes;
 } mbert_ws_layout;
 size_t mbert_workspace_bytes(const mbert_config* cfg, mbert_dtype dtype, int total_max,
                              int n_seqs);

@@ -73,6 +73,36 @@ def test_w2_padded_bf16_and_packed_equal():
     assert np.array_equal(host(pooled2), host(pooled))
 
 
+def test_w2_separate_norms_and_fold_agree():
+    """The LayerNorms run as separate kernels (the unfolded path) meet the same bar, and the
+    two paths agree closely; on the fp32 workload they agree to float rounding."""
+    wl = WORKLOADS[2]
+    b = make_batch(wl)
+    m = model_for(2)
+    ids, cu = dev_i32(b["ids"]), dev_i32(b["cu_seqlens"])
+    out_f, pool_f, _ = m.encode(ids, cu)
+    m.set_fold(False)
+    try:
+        out_s, pool_s, _ = m.encode(ids, cu)
+    finally:
+        m.set_fold(True)
+    ref, rpool = O.encode(b["ids"], b["cu_seqlens"], workload_weights(2), O.Config())
+    check_16bit(host(out_s), ref, "w2 separate norms")
+    check_16bit(host(pool_s), rpool, "w2 separate norms pooled")
+    check_16bit(host(out_f), host(out_s), "w2 folded vs separate")
+    m1 = model_for(1)
+    b1 = make_batch(WORKLOADS[1])
+    o1f, _, _ = m1.encode(dev_i32(b1["ids"]), dev_i32(b1["cu_seqlens"]))
+    m1.set_fold(False)
+    try:
+        o1s, _, _ = m1.encode(dev_i32(b1["ids"]), dev_i32(b1["cu_seqlens"]))
+    finally:
+        m1.set_fold(True)
+    e = rel_err(host(o1f), host(o1s))
+    print(f"w1 folded vs separate: rel_err={e:.3e}", flush=True)
+    assert e <= 2e-5
+
+
 def _sampled(wid):
     f = GOLD / f"oracle_samples_w{wid}.npz"
     if not f.exists():
@@ -102,13 +132,15 @@ def test_w5_32x8192_fp16():
     _sampled(5)
 
 
+@pytest.mark.parametrize("fold", [True, False], ids=["folded", "separate"])
 @pytest.mark.parametrize("lengths", [[1], [1, 2, 3], [65, 0, 129], [64, 65, 300, 7]])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_edge_batches_two_layers(lengths, dtype):
+def test_edge_batches_two_layers(lengths, dtype, fold):
     from transformer_encoder_amd.model import DeviceModel
     w = make_weights(Dims(n_layers=2), dtype, 500 + len(lengths))
     b = random_batch(lengths, 77)
-    m = DeviceModel(w, dtype)
+    m = DeviceModel(w, dtype, fold=fold)
+    assert (m.folded is not None) == fold
     out, pooled, _ = m.encode(dev_i32(b["ids"]), dev_i32(b["cu_seqlens"]))
     ref, rpool = O.encode(b["ids"], b["cu_seqlens"], w, O.Config(n_layers=2))
     if dtype == "f32":
@@ -164,12 +196,16 @@ def test_kernel_timer_counts_launches():
     pooled = t.empty((8, 768), dtype=t.float32, device="cuda")
     timer = B.mbert_timer_create(64)
     try:
-        for kind, n in ((B.K_QKV_ROPE, 22), (B.K_ATTN_GLOBAL, 8), (B.K_ATTN_LOCAL, 14),
-                        (B.K_LAYERNORM, 43)):
+        # folded LayerNorms: no separate norm kernel; separate: 21 attention + 22 MLP norms
+        for fold, kind, n in ((True, B.K_QKV_ROPE, 22), (True, B.K_ATTN_GLOBAL, 8),
+                              (True, B.K_ATTN_LOCAL, 14), (True, B.K_LAYERNORM, 0),
+                              (False, B.K_LAYERNORM, 43), (False, B.K_WI_GEGLU, 22)):
+            m.set_fold(fold)
             B.mbert_timer_reset(timer)
             B.mbert_encode_padded_timed(m.w, ids_pad, mask, 8, 512, ws, ws.numel(), out, pooled,
                                         kind, timer)
             launches, ms = B.mbert_timer_read(timer)
-            assert launches == n and ms > 0
+            assert launches == n and (ms > 0) == (n > 0)
     finally:
+        m.set_fold(True)
         B.mbert_timer_destroy(timer)

@@ -47,12 +47,14 @@ class mbert_layer_weights(Structure):
 class mbert_weights(Structure):
     _fields_ = [("cfg", mbert_config), ("dtype", c_int), ("tok_emb", c_void_p),
                 ("emb_norm", c_void_p), ("final_norm", c_void_p),
-                ("layers", POINTER(mbert_layer_weights)), ("rope", c_void_p)]
+                ("layers", POINTER(mbert_layer_weights)), ("rope", c_void_p),
+                ("folded", c_void_p)]
 
 
 class mbert_ws_layout(Structure):
     _fields_ = [(n, c_size_t) for n in ("resid", "h", "qkv", "meta", "partials", "ids", "indices",
-                                        "rowmap", "cu", "out", "total_bytes")]
+                                        "rowmap", "cu", "out", "xs", "rstats",
+                                        "total_bytes")]
 
 
 P, I, SZ = c_void_p, c_int, c_size_t
@@ -87,6 +89,8 @@ _SIGNATURES = {
     "mbert_mlm_head": ([I, P, I, P, I, P, P, c_float, P, P, I, P, SZ, P, P], I),
     "mbert_classifier_head": ([I, P, I, P, P, c_float, P, P, I, P, SZ, P, P], I),
     "mbert_workspace_bytes": ([POINTER(mbert_config), I, I, I], SZ),
+    "mbert_folded_bytes": ([POINTER(mbert_config), I], SZ),
+    "mbert_fold_norms": ([POINTER(mbert_weights), P, SZ, P], I),
     "mbert_workspace_layout": ([POINTER(mbert_config), I, I, I, POINTER(mbert_ws_layout)], I),
     "mbert_layer": ([POINTER(mbert_weights), I, I, I, P, SZ, P], I),
     "mbert_encode": ([POINTER(mbert_weights), P, P, I, I, P, SZ, P, P, P], I),
@@ -311,6 +315,14 @@ def mbert_workspace_layout(cfg, dtype, total_max, n_seqs) -> mbert_ws_layout:
     L = mbert_ws_layout()
     _call("mbert_workspace_layout", ctypes.byref(cfg), dtype, total_max, n_seqs, ctypes.byref(L))
     return L
+
+
+def mbert_folded_bytes(cfg, dtype) -> int:
+    return lib().mbert_folded_bytes(ctypes.byref(cfg), dtype)
+
+
+def mbert_fold_norms(weights, folded, nbytes, stream=None):
+    _call("mbert_fold_norms", ctypes.byref(weights), ptr(folded), nbytes, stream_handle(stream))
 
 
 def mbert_layer(weights, layer, total, n_seqs, ws, ws_bytes, stream=None):

@@ -79,6 +79,8 @@ mbert_ws_layout make_layout(mbert_dtype dt, int total_max, int n_seqs) {
     L.rowmap = take(T * 4);
     L.cu = take(((size_t)n_seqs + 1) * 4);
     L.out = take(T * D * 4);
+    L.xs = take(T * D * ds);
+    L.rstats = take(T * 12 * 8);
     L.total_bytes = off;
     return L;
 }
@@ -145,8 +147,67 @@ inline void rec_end(Recorder* r, int kind, hipStream_t s) {
         if (_rc != MBERT_OK) return _rc; \
     } while (0)
 
+// Folded weights of one layer: {Wqkv o attn_norm, c, Wi o mlp_norm, c}, 256-byte aligned.
+struct FoldLayout {
+    size_t wq, cq, wi, ci, stride;
+};
+FoldLayout fold_layout(mbert_dtype dt) {
+    FoldLayout f{};
+    const size_t wbytes = align256((size_t)QKV * D * dsize(dt)), cbytes = align256((size_t)QKV * 4);
+    f.wq = 0;
+    f.cq = wbytes;
+    f.wi = wbytes + cbytes;
+    f.ci = 2 * wbytes + cbytes;
+    f.stride = 2 * (wbytes + cbytes);
+    return f;
+}
+bool use_fold(const mbert_weights* w) { return w->folded != nullptr && w->dtype != MBERT_F16; }
+
+// One layer with the pre-norm LayerNorms folded into the QKV and Wi GEMMs: the residual
+// GEMMs leave the residual rounded to dtype (xs; for fp32 the residual itself) and its chunk
+// statistics, which the next GEMM normalises in its epilogue. Layer 0's QKV reads the
+// embedding norm output (no attention norm there); the last MLP residual feeds the final norm.
+int run_layer_folded(const mbert_weights* w, int layer, int total, int n_seqs, char* ws,
+                     const mbert_ws_layout& L, hipStream_t s, Recorder* rec) {
+    const mbert_config& c = w->cfg;
+    const mbert_layer_weights& lw = w->layers[layer];
+    const mbert_dtype dt = w->dtype;
+    const int32_t* meta = reinterpret_cast<const int32_t*>(ws + L.meta);
+    float* resid = reinterpret_cast<float*>(ws + L.resid);
+    void* h = ws + L.h;
+    void* qkv = ws + L.qkv;
+    void* xs = dt == MBERT_F32 ? nullptr : ws + L.xs;
+    const void* xa = dt == MBERT_F32 ? static_cast<const void*>(resid) : xs;  // raw residual
+    float2* st = reinterpret_cast<float2*>(ws + L.rstats);
+    const FoldLayout F = fold_layout(dt);
+    const char* fb = static_cast<const char*>(w->folded) + (size_t)layer * F.stride;
+    const bool glob = (layer % c.global_every) == 0;
+    if (layer == 0) {
+        MB_TIMED(rec, MBERT_K_QKV_ROPE, s,
+                 mbh::launch_qkv(dt, h, total, meta, lw.Wqkv, w->rope, c.max_positions, glob ? 0 : 1,
+                                 1, qkv, s));
+    } else {
+        const mbh::FoldArgs fa{reinterpret_cast<const float*>(fb + F.cq), st, c.norm_eps};
+        MB_TIMED(rec, MBERT_K_QKV_ROPE, s,
+                 mbh::launch_qkv(dt, xa, total, meta, fb + F.wq, w->rope, c.max_positions,
+                                 glob ? 0 : 1, 1, qkv, s, &fa));
+    }
+    MB_TIMED(rec, glob ? MBERT_K_ATTN_GLOBAL : MBERT_K_ATTN_LOCAL, s,
+             mbh::launch_attention(dt, qkv, total, meta, n_seqs, glob ? 1 : 0, c.half_window, h, s));
+    MB_TIMED(rec, MBERT_K_WO_RESID, s,
+             mbh::launch_linear_residual(dt, h, D, total, meta, lw.attn_Wo, resid, s, xs, st));
+    const mbh::FoldArgs fm{reinterpret_cast<const float*>(fb + F.ci), st, c.norm_eps};
+    MB_TIMED(rec, MBERT_K_WI_GEGLU, s, mbh::launch_geglu(dt, xa, total, meta, fb + F.wi, qkv, s, &fm));
+    const bool last = layer + 1 == c.n_layers;
+    MB_TIMED(rec, MBERT_K_WO2_RESID, s,
+             mbh::launch_linear_residual(dt, qkv, FF, total, meta, lw.mlp_Wo, resid, s,
+                                         last ? nullptr : xs, last ? nullptr : st));
+    return MBERT_OK;
+}
+
 int run_layer(const mbert_weights* w, int layer, int total, int n_seqs, char* ws,
-              const mbert_ws_layout& L, hipStream_t s, Recorder* rec) {
+              const mbert_ws_layout& L, hipStream_t s, Recorder* rec, bool fold = false) {
+    if (fold) return run_layer_folded(w, layer, total, n_seqs, ws, L, s, rec);
     const mbert_config& c = w->cfg;
     const mbert_layer_weights& lw = w->layers[layer];
     const mbert_dtype dt = w->dtype;
@@ -196,7 +257,8 @@ int encode_impl(const mbert_weights* w, const int32_t* ids, const int32_t* cu, i
     MB_TIMED(rec, MBERT_K_EMBED_LN, s,
              mbh::launch_embed_ln(w->dtype, ids, total, meta, w->tok_emb, w->cfg.vocab,
                                   w->emb_norm, w->cfg.norm_eps, resid, base + L.h, s));
-    for (int l = 0; l < w->cfg.n_layers; ++l) MB_TRY(run_layer(w, l, total, n_seqs, base, L, s, rec));
+    for (int l = 0; l < w->cfg.n_layers; ++l)
+        MB_TRY(run_layer(w, l, total, n_seqs, base, L, s, rec, use_fold(w)));
     MB_TIMED(rec, MBERT_K_FINAL_POOL, s,
              mbh::launch_final_ln_pool(resid, total, meta, n_seqs, w->dtype, w->final_norm,
                                        w->cfg.norm_eps, out, pooled,
@@ -224,7 +286,7 @@ int encode_padded_keymask_impl(const mbert_weights* w, const int32_t* ids_pad,
         MB_TRY(mbh::launch_embed_ln(w->dtype, ids_pad, total_max, meta, w->tok_emb, w->cfg.vocab,
                                     w->emb_norm, w->cfg.norm_eps, resid, base + L.h, s));
         for (int l = 0; l < w->cfg.n_layers; ++l)
-            MB_TRY(run_layer(w, l, total_max, B, base, L, s, nullptr));
+            MB_TRY(run_layer(w, l, total_max, B, base, L, s, nullptr, use_fold(w)));
     }
     return mbh::launch_final_ln_pool(resid, total_max, meta, B, w->dtype, w->final_norm,
                                      w->cfg.norm_eps, out_pad, pooled,
@@ -256,7 +318,7 @@ int encode_padded_impl(const mbert_weights* w, const int32_t* ids_pad, const int
                  mbh::launch_embed_ln(w->dtype, ids, total_max, meta, w->tok_emb, w->cfg.vocab,
                                       w->emb_norm, w->cfg.norm_eps, resid, base + L.h, s));
         for (int l = 0; l < w->cfg.n_layers; ++l)
-            MB_TRY(run_layer(w, l, total_max, B, base, L, s, rec));
+            MB_TRY(run_layer(w, l, total_max, B, base, L, s, rec, use_fold(w)));
     }
     MB_TIMED(rec, MBERT_K_FINAL_POOL, s,
              mbh::launch_final_ln_pool(resid, total_max, meta, B, w->dtype, w->final_norm,
@@ -619,6 +681,30 @@ int mbert_workspace_layout(const mbert_config* c, mbert_dtype dt, int total_max,
     MB_TRY(check_sizes(total_max, n_seqs));
     if (!layout) return MBERT_EINVAL;
     *layout = make_layout(dt, total_max, n_seqs);
+    return MBERT_OK;
+}
+
+size_t mbert_folded_bytes(const mbert_config* c, mbert_dtype dt) {
+    if (check_cfg(c) || check_dtype(dt) || dt == MBERT_F16) return 0;
+    return fold_layout(dt).stride * (size_t)c->n_layers;
+}
+
+int mbert_fold_norms(const mbert_weights* w, void* folded, size_t bytes, void* stream) {
+    MB_TRY(check_weights(w));
+    if (w->dtype == MBERT_F16) return MBERT_EUNSUPPORTED;
+    if (!folded) return MBERT_EINVAL;
+    if (bytes < mbert_folded_bytes(&w->cfg, w->dtype)) return MBERT_ENOSPC;
+    const FoldLayout F = fold_layout(w->dtype);
+    hipStream_t s = as_stream(stream);
+    for (int l = 0; l < w->cfg.n_layers; ++l) {
+        char* fb = static_cast<char*>(folded) + (size_t)l * F.stride;
+        const mbert_layer_weights& lw = w->layers[l];
+        if (l > 0)
+            MB_TRY(mbh::launch_fold_weight(w->dtype, lw.Wqkv, lw.attn_norm, QKV, fb + F.wq,
+                                           reinterpret_cast<float*>(fb + F.cq), s));
+        MB_TRY(mbh::launch_fold_weight(w->dtype, lw.Wi, lw.mlp_norm, 2 * FF, fb + F.wi,
+                                       reinterpret_cast<float*>(fb + F.ci), s));
+    }
     return MBERT_OK;
 }
 

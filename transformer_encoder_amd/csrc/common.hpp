@@ -180,15 +180,29 @@ int launch_attention_probs(mbert_dtype dt, const void* qkv, int row0, int n_q, i
 int launch_final_ln_pool(const float* resid, int total, const int32_t* meta, int n_seqs,
                          mbert_dtype dt, const void* w, float eps, float* out, float* pooled,
                          float* partials, hipStream_t s);
+// A LayerNorm folded into the GEMM that follows it: the A operand is the raw residual (in
+// dtype; the fp32 residual itself for MBERT_F32), W is the folded weight (W o w), and the
+// epilogue applies rstd * (acc - mean * c) from the producer's chunk statistics.
+struct FoldArgs {
+    const float* c;        // [rows of W]
+    const float2* stats;   // [rows][12] {mean, M2} per 64-column chunk
+    float eps;
+};
 int launch_qkv(mbert_dtype dt, const void* h, int total, const int32_t* meta, const void* W,
                const float* rope, int max_pos, int table, int apply_rope, void* qkv,
-               hipStream_t s);
+               hipStream_t s, const FoldArgs* fold = nullptr);
+// Folded weight of one norm: Wf [rows,768] = W o w rounded to dtype, c [rows] = row sums of Wf.
+int launch_fold_weight(mbert_dtype dt, const void* W, const void* w, int rows, void* Wf,
+                       float* c, hipStream_t s);
 int launch_rope(mbert_dtype dt, void* qkv, int total, const int32_t* meta, const float* rope,
                 int max_pos, int table, hipStream_t s);
+// With stats_out, the residual epilogue also writes the new residual's chunk statistics and
+// (xs_out, 16-bit types) the residual rounded to dtype, for a folded LayerNorm next.
 int launch_linear_residual(mbert_dtype dt, const void* a, int K, int total, const int32_t* meta,
-                           const void* W, float* resid, hipStream_t s);
+                           const void* W, float* resid, hipStream_t s, void* xs_out = nullptr,
+                           float2* stats_out = nullptr);
 int launch_geglu(mbert_dtype dt, const void* h, int total, const int32_t* meta, const void* Wi,
-                 void* m, hipStream_t s);
+                 void* m, hipStream_t s, const FoldArgs* fold = nullptr);
 int launch_attention(mbert_dtype dt, const void* qkv, int total, const int32_t* meta, int n_seqs,
                      int is_global, int W, void* o, hipStream_t s);
 }  // namespace mbh

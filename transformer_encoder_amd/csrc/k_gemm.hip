@@ -96,6 +96,7 @@ namespace mb {
 enum { EPI_STORE = 0, EPI_ROPE = 1, EPI_RESID = 2, EPI_GEGLU = 3, EPI_GELU_F32 = 4, EPI_BIAS_F32 = 5 };
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 struct GemmArgs {
     const void* A;       // [M, K] dtype
@@ -109,6 +110,16 @@ struct GemmArgs {
     const float2* rope;  // ROPE: {cos, sin} table [max_pos][32] of the layer kind
     int max_pos;
     const void* bias;    // BIAS_F32: [N] dtype
+    // LayerNorm folded into this GEMM (STORE / ROPE / GEGLU): A holds the raw residual in
+    // dtype and B the weight with its columns scaled by the norm weight, W o w; the output is
+    // rstd * (acc - mean * cfold[col]), mean and rstd merged from stats_in. Off when null.
+    const float* cfold;      // [rows of B] sums over k of (W o w)[row][k]
+    const float2* stats_in;  // [M][NCHUNK] {mean, M2} of each 64-column chunk of each row
+    float eps;
+    // RESID extras: the new residual rounded to dtype (xs_out, [M, 768], may be null) and its
+    // per-chunk statistics (stats_out) for the next folded GEMM. Off when stats_out is null.
+    void* xs_out;
+    float2* stats_out;
 };
 
 template <typename T> struct MfmaOp;
@@ -257,6 +268,28 @@ __device__ __forceinline__ int b_row(int bn, int r) {
     }
 }
 
+// Residual statistics come in 64-column chunks: 12 per 768-wide row.
+constexpr int NCHUNK = 768 / 64;
+
+// Sum over each row of 16 lanes (the same value in all 16), by DPP lane swaps.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f<0x141>(v);  // row_half_mirror
+    v += dpp_f<0x140>(v);  // row_mirror
+    return v;
+}
+
+__device__ __forceinline__ void buf_store8b(unsigned long long v, const void* base, unsigned extent,
+                                            unsigned off) {
+#if __HIP_DEVICE_COMPILE__
+    __builtin_amdgcn_raw_buffer_store_b64(
+        __builtin_bit_cast(u32x2, v),
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, extent, 0x00020000),
+        off, 0, 0);
+#endif
+}
+
 // 16-byte store through a buffer descriptor (base, extent in bytes): a store at or beyond the
 // extent is dropped by the hardware, so rows past the end need no branch (a branch around a
 // store leaves the compiler unsure how many stores are in flight, and it then waits for all).
@@ -307,7 +340,9 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     constexpr int EROWS = NWM * 32;                       // rows staged per epilogue pass
     constexpr int MAIN_BYTES = (DS > 0 ? DS : 2) * (BM + BN) * ROWB;
     constexpr int EPI_BYTES = EROWS * CP * 4;
-    constexpr int SMEM = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+    // epilogue: the staged rows, then (folded GEMMs) {mean, rstd} per tile row and c per column
+    constexpr int EPI_ALL = EPI_BYTES + BM * 8 + BN * 4;
+    constexpr int SMEM = MAIN_BYTES > EPI_ALL ? MAIN_BYTES : EPI_ALL;
     static_assert(EPI != EPI_ROPE || BN % 64 == 0, "RoPE tiles hold whole heads");
     static_assert(BM % RSTEP == 0 && BN % RSTEP == 0, "tile rows must split over the threads");
     __shared__ __align__(16) unsigned char smem[SMEM];
@@ -331,18 +366,35 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     float4 rcs[2][R_IT][4];
     f32x4 rold[2][S_IT];
     float4 fbias[EPI == EPI_BIAS_F32 ? (NWM * 32) * S_CH / (64 * NWM * NWN) : 1];
-    if constexpr (EPI == EPI_ROPE) {
+    if constexpr (EPI == EPI_ROPE) {  // raw positions; clamped after the main loop
 #pragma unroll
         for (int i = 0; i < (BM / NWM) / 32; ++i)
 #pragma unroll
             for (int k = 0; k < R_IT; ++k) {
                 const int sr = (tid0 + 64 * NWM * NWN * k) / (4 * R_NHT);
-                rpos[i][k] = min(max(p.pos[min(tile_row_of(i, sr), M - 1)], 0), p.max_pos - 1);
+                rpos[i][k] = p.pos[min(tile_row_of(i, sr), M - 1)];
             }
     } else if constexpr (EPI == EPI_BIAS_F32) {
 #pragma unroll
         for (int k = 0; k < (int)(sizeof(fbias) / sizeof(fbias[0])); ++k)
             fbias[k] = Vec4<T>::load((const T*)p.bias + bn * BN + 4 * ((tid0 + 64 * NWM * NWN * k) % S_CH));
+    }
+    // Folded LayerNorm: this tile's row statistics and column sums are loaded now (they are
+    // used after the main loop, so the loads are in flight behind it)
+    constexpr bool FOLDABLE = EPI == EPI_STORE || EPI == EPI_ROPE || EPI == EPI_GEGLU;
+    const bool fold = FOLDABLE && p.stats_in != nullptr;
+    // (unconditional loads, from the weights when there is no fold, so that no branch stands
+    // between them and the main loop's wait counts)
+    float2 fst[NCHUNK];
+    float fc = 0.f;
+    if constexpr (FOLDABLE) {
+        static_assert(BM <= 64 * NWM * NWN && BN <= 64 * NWM * NWN, "a thread per row and column");
+        const float2* sp = fold ? p.stats_in : reinterpret_cast<const float2*>(p.B);
+        const float* cp = fold ? p.cfold : reinterpret_cast<const float*>(p.B);
+        const int r = fold ? min(m0 + min(tid0, BM - 1), M - 1) : 0;
+#pragma unroll
+        for (int j = 0; j < NCHUNK; ++j) fst[j] = sp[(size_t)r * NCHUNK + j];
+        fc = cp[fold ? b_row<EPI, BN>(bn, min(tid0, BN - 1)) : 0];
     }
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -597,6 +649,11 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                      : p.N * 4;
     const void* cbase = (const unsigned char*)p.C + (size_t)m0 * cpitch;
     const unsigned cext = (unsigned)min((size_t)(M - m0) * cpitch, (size_t)0xFFFFFFFFu);
+    // residual extras: statistics [M][NCHUNK] float2 and the dtype copy [M, 768]
+    const void* sbase = (const unsigned char*)p.stats_out + (size_t)m0 * NCHUNK * 8;
+    const unsigned sext = (unsigned)min((size_t)(M - m0) * NCHUNK * 8, (size_t)0xFFFFFFFFu);
+    const void* xbase = (const unsigned char*)p.xs_out + (size_t)m0 * D * sizeof(T);
+    const unsigned xext = (unsigned)min((size_t)(M - m0) * D * sizeof(T), (size_t)0xFFFFFFFFu);
     auto issue_loads = [&](int i) {
         if constexpr (EPI == EPI_ROPE) {  // value tiles load (and ignore) the table too
 #pragma unroll
@@ -614,6 +671,50 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                     (const float*)p.C + (size_t)min(tile_row_of(i, sr), M - 1) * D + bn * BN + 4 * c);
             }
         }
+    };
+    // Values loaded before the main loop are first used here: the empty asm statements keep
+    // the compiler from starting their arithmetic (and so waiting for them) before the loop.
+    if constexpr (EPI == EPI_ROPE) {
+#pragma unroll
+        for (int i = 0; i < (BM / NWM) / 32; ++i)
+#pragma unroll
+            for (int k = 0; k < R_IT; ++k) {
+                asm volatile("" : "+v"(rpos[i][k]));
+                rpos[i][k] = min(max(rpos[i][k], 0), p.max_pos - 1);
+            }
+    }
+    if constexpr (FOLDABLE) {
+#pragma unroll
+        for (int j = 0; j < NCHUNK; ++j) asm volatile("" : "+v"(fst[j].x), "+v"(fst[j].y));
+        asm volatile("" : "+v"(fc));
+    }
+    float2* rowstat = reinterpret_cast<float2*>(smem + EPI_BYTES);     // [BM] {mean, rstd}
+    float* cst = reinterpret_cast<float*>(smem + EPI_BYTES + BM * 8);  // [BN]
+    if constexpr (FOLDABLE) {
+        if (fold) {
+            // Chan et al.'s pairwise merge of the 12 chunk statistics (equal counts of 64):
+            // mean = mean of the means, M2 = sum of M2 + 64 * sum of squared mean deviations;
+            // biased variance M2 / 768, eps inside the square root, as the LayerNorm kernel
+            float mean = 0.f;
+#pragma unroll
+            for (int j = 0; j < NCHUNK; ++j) mean += fst[j].x;
+            mean *= 1.0f / NCHUNK;
+            float m2 = 0.f, dev = 0.f;
+#pragma unroll
+            for (int j = 0; j < NCHUNK; ++j) {
+                m2 += fst[j].y;
+                dev += (fst[j].x - mean) * (fst[j].x - mean);
+            }
+            const float var = (m2 + 64.0f * dev) * (1.0f / D);
+            if (tid < BM) rowstat[tid] = make_float2(mean, 1.0f / sqrtf(var + p.eps));
+            if (tid < BN) cst[tid] = fc;
+        }
+    }
+    // out = rstd * (acc - mean * c) for tile row tr (0 .. BM-1) and tile column tc
+    auto fold8 = [&](float* v, int tr, int tc) {
+        const float2 st = rowstat[tr];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = (v[q] - st.x * cst[tc + q]) * st.y;
     };
     issue_loads(0);
 #pragma unroll
@@ -634,6 +735,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 const int idx = tid + NT * k, sr = idx / CH, c = idx % CH, row = tile_row(sr);
                 float v[8];
                 load8(Cs + sr * CP + 8 * c, v);
+                if (fold) fold8(v, row - m0, 8 * c);
                 buf_store8<T>(cbase, cext, (unsigned)((row - m0) * cpitch + (bn * BN + 8 * c) * (int)sizeof(T)), v);
             }
         } else if constexpr (EPI == EPI_ROPE) {
@@ -646,6 +748,10 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 const float* x = Cs + sr * CP + HD * hh + 8 * pc;
                 load8(x, x1);
                 load8(x + 32, x2);
+                if (fold) {
+                    fold8(x1, row - m0, HD * hh + 8 * pc);
+                    fold8(x2, row - m0, HD * hh + 8 * pc + 32);
+                }
                 if (rot) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
@@ -669,6 +775,25 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 const f32x4 v = rold[i & 1][k] + a;
                 buf_store16(__builtin_bit_cast(u32x4, v), cbase, cext,
                             (unsigned)(((row - m0) * D + bn * BN + 4 * c) * 4));
+                if (p.stats_out) {
+                    // the 16 lanes of this DPP row hold one 64-column chunk of this row:
+                    // its mean, then the sum of squared deviations from it (two passes)
+                    const float mean = row16_sum((v.x + v.y) + (v.z + v.w)) * (1.0f / 64);
+                    const f32x4 d = v - mean;
+                    const float m2 = row16_sum((d.x * d.x + d.y * d.y) + (d.z * d.z + d.w * d.w));
+                    if ((lane & 15) == 0)
+                        buf_store8b(__builtin_bit_cast(unsigned long long, make_float2(mean, m2)),
+                                    sbase, sext,
+                                    (unsigned)(((row - m0) * NCHUNK + (bn * BN + 4 * c) / 64) * 8));
+                    if constexpr (sizeof(T) == 2) {
+                        if (p.xs_out) {
+                            typedef T t4 __attribute__((ext_vector_type(4)));
+                            const t4 o = {(T)v.x, (T)v.y, (T)v.z, (T)v.w};
+                            buf_store8b(__builtin_bit_cast(unsigned long long, o), xbase, xext,
+                                        (unsigned)(((row - m0) * D + bn * BN + 4 * c) * 2));
+                        }
+                    }
+                }
             }
         } else if constexpr (EPI == EPI_GELU_F32 || EPI == EPI_BIAS_F32) {
             constexpr int CH = BN / 4, IT = EROWS * CH / NT;
@@ -700,6 +825,10 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 float g[8], u[8];
                 load8(Cs + sr * CP + 8 * c, g);
                 load8(Cs + sr * CP + HALF + 8 * c, u);
+                if (fold) {
+                    fold8(g, row - m0, 8 * c);
+                    fold8(u, row - m0, HALF + 8 * c);
+                }
 #pragma unroll
                 for (int q = 0; q < 8; ++q) g[q] = gelu_erf(g[q]) * u[q];
                 buf_store8<T>(cbase, cext, (unsigned)((row - m0) * cpitch + (bn * HALF + 8 * c) * (int)sizeof(T)), g);
@@ -773,8 +902,13 @@ using namespace mb;
 
 int launch_qkv(mbert_dtype dt, const void* h, int total, const int32_t* meta, const void* W,
                const float* rope, int max_pos, int table, int apply_rope, void* qkv,
-               hipStream_t s) {
+               hipStream_t s, const FoldArgs* fold) {
     GemmArgs a{};
+    if (fold) {
+        a.cfold = fold->c;
+        a.stats_in = fold->stats;
+        a.eps = fold->eps;
+    }
     a.A = h;
     a.B = W;
     a.M = total;
@@ -794,8 +928,11 @@ int launch_qkv(mbert_dtype dt, const void* h, int total, const int32_t* meta, co
 }
 
 int launch_linear_residual(mbert_dtype dt, const void* a_, int K, int total, const int32_t* meta,
-                           const void* W, float* resid, hipStream_t s) {
+                           const void* W, float* resid, hipStream_t s, void* xs_out,
+                           float2* stats_out) {
     GemmArgs a{};
+    a.xs_out = xs_out;
+    a.stats_out = stats_out;
     a.A = a_;
     a.B = W;
     a.M = total;
@@ -812,8 +949,13 @@ int launch_linear_residual(mbert_dtype dt, const void* a_, int K, int total, con
 }
 
 int launch_geglu(mbert_dtype dt, const void* h, int total, const int32_t* meta, const void* Wi,
-                 void* m, hipStream_t s) {
+                 void* m, hipStream_t s, const FoldArgs* fold) {
     GemmArgs a{};
+    if (fold) {
+        a.cfold = fold->c;
+        a.stats_in = fold->stats;
+        a.eps = fold->eps;
+    }
     a.A = h;
     a.B = Wi;
     a.M = total;
@@ -855,5 +997,49 @@ int launch_linear_f32(mbert_dtype dt, const void* a_, int M, const void* W, int 
                         : mb::run_gemm_f32<mb::f16, mb::EPI_BIAS_F32>(a, s);
         default: return MBERT_EUNSUPPORTED;
     }
+}
+}  // namespace mbh
+
+namespace mb {
+// Folded LayerNorm weight: Wf[r][k] = W[r][k] * w[k] rounded once to T, and c[r] the sum of
+// the rounded row (so that rstd * (x . Wf_r - mean * c_r) is exactly sum_k (x_k - mean) rstd
+// w_k W_rk up to the rounding of Wf). One wave per row, a fixed summation order.
+template <typename T>
+__global__ __launch_bounds__(256) void fold_weight_kernel(const T* __restrict__ W,
+                                                          const T* __restrict__ w, int rows,
+                                                          T* __restrict__ Wf, float* __restrict__ c) {
+    const int lane = threadIdx.x & 63, r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) {
+        const int k = lane + 64 * j;
+        const T v = (T)(to_f(W[(size_t)r * D + k]) * to_f(w[k]));
+        Wf[(size_t)r * D + k] = v;
+        acc += to_f(v);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) c[r] = acc;
+}
+}  // namespace mb
+
+namespace mbh {
+int launch_fold_weight(mbert_dtype dt, const void* W, const void* w, int rows, void* Wf,
+                       float* c, hipStream_t s) {
+    const unsigned grid = (unsigned)((rows + 3) / 4);
+    switch (dt) {
+        case MBERT_F32:
+            MB_LAUNCH((mb::fold_weight_kernel<float>), grid, 256, 0, s, (const float*)W, (const float*)w, rows,
+                      (float*)Wf, c);
+            break;
+        case MBERT_BF16:
+            MB_LAUNCH((mb::fold_weight_kernel<mb::bf16>), grid, 256, 0, s, (const mb::bf16*)W,
+                      (const mb::bf16*)w, rows, (mb::bf16*)Wf, c);
+            break;
+        default:
+            return MBERT_EUNSUPPORTED;
+    }
+    MB_CHECK_LAUNCH();
+    return MBERT_OK;
 }
 }  // namespace mbh

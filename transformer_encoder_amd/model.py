@@ -34,7 +34,7 @@ def int32_device(a, device="cuda"):
 
 class DeviceModel:
     def __init__(self, weights: dict, dtype: str, device="cuda", cfg: B.mbert_config | None = None,
-                 stream=None):
+                 stream=None, fold: bool = True):
         import torch
         self.dtype_name = dtype
         self.dtype = B.DTYPES[dtype]
@@ -72,6 +72,17 @@ class DeviceModel:
         self.w.final_norm = B.ptr(self.final_norm)
         self.w.layers = ctypes.cast(self.layers_c, ctypes.POINTER(B.mbert_layer_weights))
         self.w.rope = B.ptr(self.rope)
+        # LayerNorms folded into the following GEMMs (bf16 and fp32; fp16 runs them apart)
+        self.folded = None
+        nb = B.mbert_folded_bytes(self.cfg, self.dtype)
+        if fold and nb > 0:
+            self.folded = torch.empty(nb, dtype=torch.uint8, device=device)
+            B.mbert_fold_norms(self.w, self.folded, nb, stream)
+            self.w.folded = B.ptr(self.folded)
+
+    def set_fold(self, on: bool):
+        """Switch the forward between folded and separate LayerNorms (if folded weights exist)."""
+        self.w.folded = B.ptr(self.folded) if (on and self.folded is not None) else None
 
     def workspace(self, total_max: int, n_seqs: int):
         import torch
