@@ -68,7 +68,7 @@ template <> struct Vec4<f16> {
 // added in row order.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
 }
 __device__ __forceinline__ float wave_sum(float v) {
     v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
