@@ -4,14 +4,13 @@
 // Main loop: 4 (or 8) wave64s in a 2x2 (2x4) arrangement; each wave owns a sub-tile made of
 // 32x32 MFMA blocks (v_mfma_f32_32x32x16_{bf16,f16}; fp32 inputs use v_mfma_f32_32x32x2_f32,
 // four per 16-byte operand). K is consumed 128 bytes at a time (64 16-bit or 32 fp32
-// elements); K is only 768 or 1152, so a workgroup's whole life is a dozen K-steps and the
-// load latency has to be covered by loads in flight, not by a long loop. Operand tiles go
-// from global memory straight into LDS (global_load_lds, 16 bytes per lane), DS - 1 K-steps
-// ahead of the MFMAs, with explicit wait counts and one raw barrier per K-step; a register-
-// staged variant (loads P K-steps ahead into registers, stored to two LDS stages) is kept as a
-// compile-time option. LDS rows are unpadded and XOR-swizzled by 16-byte chunk (see lds_off),
-// which keeps the 16-byte operand reads conflict-free. All fragments of a K-step are read
-// before its MFMAs.
+// elements; 64 bytes is a compile-time option); K is only 768 or 1152, so a workgroup's whole
+// life is a dozen K-steps and the load latency has to be covered by loads in flight, not by a
+// long loop. Operand tiles go from global memory straight into LDS (buffer loads with the LDS
+// destination, 16 bytes per lane) into DS stages, with explicit wait counts and one raw
+// barrier per K-step. LDS rows are unpadded and XOR-swizzled by 16-byte chunk (see lds_off),
+// which keeps the 16-byte operand reads conflict-free. The fragment reads are software-
+// pipelined: those of k-substep s + 1 are issued before the MFMAs of substep s.
 //
 // Epilogue: the fp32 accumulator tile is staged through LDS (row pitch BN + 8 floats, which
 // keeps the two half-waves of an MFMA block on disjoint banks) and then processed row-major,
@@ -28,31 +27,23 @@
 //   GELU_F32 / BIAS_F32 : C (fp32, row pitch N) = gelu_erf(acc) or acc + bias[col], the dense
 //           layer of the prediction head and the biased decoder / classifier Linear
 //           (kgptalkie, §"The Masked-LM Head")
-// Epilogues that read memory issue all their loads first, from rows clamped into range.
+// Epilogues that read memory issue all their loads first, from rows clamped into range, and
+// each pass issues the next pass's loads before its own stores; stores go through buffer
+// descriptors that drop rows past the end. With a folded LayerNorm (cfold / stats_in) the
+// accumulators are normalised first, rstd * (acc - mean * c); the residual epilogue can also
+// write the new residual's chunk statistics and its dtype copy for the next such GEMM.
 // Work distribution: tiles are spread over the 8 XCDs in contiguous ranges counted from the
 // real row count read on the device (the padded path sizes its grid for B * Tpad rows).
 #include "common.hpp"
 
-// Operand staging: the number of LDS stages filled straight from global memory, or 0 for the
-// register-staged prefetch. Measured on whole forwards of the padded batch-8 workload (graph
-// replay): register staging everywhere 1.870 ms, two direct stages everywhere 1.914 ms, two for
-// the 2304-wide GEMMs and register staging for the 768-wide ones 1.809 ms, two and three
-// 1.795 ms. (Two direct stages are 5-15 % faster than register staging on the 2304-wide GEMMs
-// alone at 1k-32k rows.)
+// Operand staging: the number of LDS stages per tile shape (two for the 2304-wide GEMMs, three
+// for the 768-wide ones, measured on whole forwards of the padded batch-8 workload; deeper
+// stages or 64-byte K-steps were slower at 1k-262k rows).
 #ifndef MB_GEMM_DMA
 #define MB_GEMM_DMA 2
 #endif
 #ifndef MB_GEMM_DMA_N768
 #define MB_GEMM_DMA_N768 3
-#endif
-#ifndef MB_GEMM_BUFLDS
-#define MB_GEMM_BUFLDS 1
-#endif
-#ifndef MB_GEMM_PIPE
-#define MB_GEMM_PIPE 1
-#endif
-#ifndef MB_GEMM_BIG_NWN
-#define MB_GEMM_BIG_NWN 4
 #endif
 #ifndef MB_GEMM_MID_DS
 #define MB_GEMM_MID_DS MB_GEMM_DMA
@@ -161,18 +152,12 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane i's bytes land at lds + 16 i
-// (lds is the same for the whole wave). The builtin exists only for the device target; the
-// host pass, which never runs this, would otherwise drop every kernel that uses it.
-__device__ __forceinline__ void lds_dma16(const unsigned char* g, unsigned char* lds) {
-#if __HIP_DEVICE_COMPILE__
-    __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
-#endif
-}
-
-// The same through a buffer load (MUBUF, offset = voff + soff from an SGPR base): wait counts
-// for LDS reads then stay exact per instruction, where a global (FLAT) load into LDS makes the
-// compiler wait for every LDS operation before any use.
+// 16 bytes per lane from global memory straight into LDS through a buffer load (MUBUF, offset
+// = voff + soff from an SGPR base): lane i's bytes land at lds + 16 i (lds is the same for the
+// whole wave). A buffer load, not a global (FLAT) one: after a FLAT load into LDS the compiler
+// waits for every LDS operation before any use, with this one its LDS wait counts stay exact.
+// The builtin exists only for the device target; the host pass, which never runs this, would
+// otherwise drop every kernel that uses it.
 __device__ __forceinline__ void lds_dma16_buf(const void* base, unsigned extent, unsigned voff,
                                               unsigned soff, unsigned char* lds) {
 #if __HIP_DEVICE_COMPILE__
@@ -321,30 +306,25 @@ __device__ __forceinline__ void load8(const float* src, float* v) {
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int P, int OCC, int DS = 0,
-          int RB = 128>
+template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int OCC, int DS, int RB = 128>
 __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
-    // DS > 0: operand tiles go from global memory straight into DS LDS stages
-    // (global_load_lds, 16 bytes per lane), DS - 1 K-steps ahead, with explicit wait counts and
-    // raw barriers; DS == 0: register-staged prefetch P K-steps ahead into two LDS stages.
-    // RB: bytes of K per row and K-step (128, or 64 for more stages in the same LDS).
+    // Operand tiles go from global memory straight into DS LDS stages (16 bytes per lane),
+    // with explicit wait counts and raw barriers. RB: bytes of K per row and K-step (128, or
+    // 64 for more stages in the same LDS).
     constexpr int NT = 64 * NWM * NWN;                    // threads
     constexpr int ROWB = RB;   // bytes of K per row per stage; rows are unpadded (swizzled)
-    static_assert(RB == 128 || (RB == 64 && DS > 0), "64-byte K-steps need direct staging");
+    static_assert(RB == 128 || RB == 64, "K-steps of 128 or 64 bytes");
     constexpr int SUB = ROWB / 32;                        // MFMA k-substeps per K-step
     constexpr int KT = ROWB / (int)sizeof(T);
     constexpr int WM = BM / NWM, WN = BN / NWN, FM = WM / 32, FN = WN / 32;
-    constexpr int RSTEP = NT / 8;                         // rows per 16-byte-chunk pass
-    constexpr int ACH = BM / RSTEP, BCH = BN / RSTEP;
     constexpr int CP = BN + 8;                            // epilogue staging pitch (floats)
     constexpr int EROWS = NWM * 32;                       // rows staged per epilogue pass
-    constexpr int MAIN_BYTES = (DS > 0 ? DS : 2) * (BM + BN) * ROWB;
+    constexpr int MAIN_BYTES = DS * (BM + BN) * ROWB;
     constexpr int EPI_BYTES = EROWS * CP * 4;
     // epilogue: the staged rows, then (folded GEMMs) {mean, rstd} per tile row and c per column
     constexpr int EPI_ALL = EPI_BYTES + BM * 8 + BN * 4;
     constexpr int SMEM = MAIN_BYTES > EPI_ALL ? MAIN_BYTES : EPI_ALL;
     static_assert(EPI != EPI_ROPE || BN % 64 == 0, "RoPE tiles hold whole heads");
-    static_assert(BM % RSTEP == 0 && BN % RSTEP == 0, "tile rows must split over the threads");
     __shared__ __align__(16) unsigned char smem[SMEM];
 
     const int nbn = p.N / BN;
@@ -399,7 +379,6 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / NWN, wn = wave % NWN;
-    const int crow = tid >> 3, cchunk = tid & 7;
     const size_t ld = (size_t)p.K * sizeof(T);
 
     f32x16 acc[FM][FN];
@@ -412,7 +391,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
 
     const int nk = p.K / KT;
     const int lrow = lane & 31, lk = lane >> 5;  // lk: which 16-byte half of a 32-byte k-step
-    if constexpr (DS > 0) {
+    static_assert(DS >= 2, "at least two LDS stages");
     constexpr int NW = NWM * NWN;
     constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
     constexpr int RPG = 64 / CPR;         // rows per 1 KB group (one DMA instruction)
@@ -423,9 +402,8 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     // Group g covers LDS rows RPG*g .. RPG*g + RPG-1 (A rows first, then B rows); lane L fills
     // row RPG*g + L/CPR at physical chunk L%CPR, which holds the logical chunk that lds_off
     // places there (the swizzle is its own inverse).
-#if MB_GEMM_BUFLDS
-    // Buffer form: A groups (the first AJ of each wave) read from this tile's first row, B
-    // groups from the weight base; offsets are 32-bit and stay inside each extent (rows are
+    // A groups (the first AJ of each wave) read from this tile's first row, B groups from the
+    // weight base; offsets are 32-bit and stay inside each extent (rows are
     // clamped), the K-step goes into the scalar offset.
     constexpr int AJ = (BM / RPG) / NW;
     static_assert((BM / RPG) % NW == 0, "A and B groups split evenly over the waves");
@@ -448,28 +426,6 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                           voff[jg], (unsigned)(KT_) * ROWB,                               \
                           smem + (ST_) * STAGE + (wu + NW * jg) * 1024);                  \
     } while (0)
-#else
-    const unsigned char* gsrc[GW];
-#pragma unroll
-    for (int jg = 0; jg < GW; ++jg) {
-        const int g = wave + NW * jg, lrow8 = RPG * g + lane / CPR;
-        const int c = (lds_off<ROWB>(lrow8, lane % CPR) - lrow8 * ROWB) >> 4;
-        if (g < BM / RPG) {
-            const int gr = min(m0 + lrow8, M - 1);
-            gsrc[jg] = (const unsigned char*)p.A + (size_t)gr * ld + c * 16;
-        } else {
-            const int gr = b_row<EPI, BN>(bn, lrow8 - BM);
-            gsrc[jg] = (const unsigned char*)p.B + (size_t)gr * ld + c * 16;
-        }
-    }
-#define MB_DMA(KT_, ST_)                                                                  \
-    do {                                                                                  \
-        _Pragma("unroll") for (int jg = 0; jg < GW; ++jg)                                 \
-            lds_dma16(gsrc[jg] + (size_t)(KT_) * ROWB,                                    \
-                      smem + (ST_) * STAGE + (wave + NW * jg) * 1024);                    \
-    } while (0)
-#endif
-#if MB_GEMM_PIPE
 #define MB_FRAGS(ST_, S_, B_)                                                              \
     do {                                                                                  \
         _Pragma("unroll") for (int i = 0; i < FM; ++i) af[B_][i] =                        \
@@ -518,38 +474,6 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
         }
     }
 #undef MB_FRAGS
-#else
-#pragma unroll
-    for (int st = 0; st < DS - 1; ++st) MB_DMA(min(st, nk - 1), st);
-    for (int kt = 0; kt < nk; ++kt) {
-        // this wave's DMAs for K-step kt are done once at most GW * (DS - 2) are in flight
-        // (loads complete in order); the barrier then makes every wave's part visible and
-        // frees the stage read in the previous step for the next DMA
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(GW * (DS - 2)));
-        __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        MB_DMA(min(kt + DS - 1, nk - 1), (kt + DS - 1) % DS);
-        const unsigned char* St = smem + (kt % DS) * STAGE;
-        u32x4 af[SUB][FM], bf[SUB][FN];
-#pragma unroll
-        for (int s = 0; s < SUB; ++s) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[s][i] = *(const u32x4*)(St + lds_off<ROWB>(wm * WM + 32 * i + lrow, 2 * s + lk));
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                bf[s][j] = *(const u32x4*)(St + lds_off<ROWB>(BM + wn * WN + 32 * j + lrow, 2 * s + lk));
-        }
-#pragma unroll
-        for (int s = 0; s < SUB; ++s)
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) MfmaOp<T>::run(af[s][i], bf[s][j], acc[i][j]);
-    }
-#endif
 #undef MB_DMA
     // the last DMAs (re-reads of the last K-step) land before the epilogue reuses the LDS
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -557,79 +481,6 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    } else {
-    const unsigned char* a_ptr[ACH];
-    const unsigned char* b_ptr[BCH];
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-        const int gr = min(m0 + crow + RSTEP * i, M - 1);
-        a_ptr[i] = (const unsigned char*)p.A + (size_t)gr * ld + cchunk * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-        const int gr = b_row<EPI, BN>(bn, crow + RSTEP * i);
-        b_ptr[i] = (const unsigned char*)p.B + (size_t)gr * ld + cchunk * 16;
-    }
-
-    u32x4 ra[P][ACH], rb[P][BCH];
-
-
-#define MB_GLOAD(KT_, U_)                                                                 \
-    do {                                                                                  \
-        const size_t off_ = (size_t)(KT_) * ROWB;                                         \
-        _Pragma("unroll") for (int i = 0; i < ACH; ++i) ra[U_][i] = *(const u32x4*)(a_ptr[i] + off_); \
-        _Pragma("unroll") for (int i = 0; i < BCH; ++i) rb[U_][i] = *(const u32x4*)(b_ptr[i] + off_); \
-    } while (0)
-#define MB_SSTORE(U_, ST_)                                                                \
-    do {                                                                                  \
-        unsigned char* base_ = smem + (ST_) * (BM + BN) * ROWB;                           \
-        _Pragma("unroll") for (int i = 0; i < ACH; ++i)                                   \
-            *(u32x4*)(base_ + lds_off(crow + RSTEP * i, cchunk)) = ra[U_][i];             \
-        _Pragma("unroll") for (int i = 0; i < BCH; ++i)                                   \
-            *(u32x4*)(base_ + lds_off(BM + crow + RSTEP * i, cchunk)) = rb[U_][i];        \
-    } while (0)
-
-    // Every load is unconditional (the tail re-reads the last K-tile, whose data is never
-    // used): a load issued under a branch leaves the wait-count pass unsure how many loads are
-    // in flight, and it then waits for all of them, prefetch included. nk % P == 0 (checked
-    // on the host), so the unrolled loop needs no guards either.
-#pragma unroll
-    for (int u = 0; u < P; ++u) MB_GLOAD(min(u, nk - 1), u);
-    MB_SSTORE(0, 0);
-    __syncthreads();
-    for (int kt0 = 0; kt0 < nk; kt0 += P) {
-#pragma unroll
-        for (int u = 0; u < P; ++u) {
-            const int kt = kt0 + u;
-            MB_GLOAD(min(kt + P, nk - 1), u);
-            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch at the head of the K-step
-            const unsigned char* St = smem + (kt & 1) * (BM + BN) * ROWB;
-            // all operand fragments of the K-step are read first, then the MFMAs run back to
-            // back as the reads land
-            u32x4 af[4][FM], bf[4][FN];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    af[s][i] = *(const u32x4*)(St + lds_off(wm * WM + 32 * i + lrow, 2 * s + lk));
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    bf[s][j] = *(const u32x4*)(St + lds_off(BM + wn * WN + 32 * j + lrow, 2 * s + lk));
-            }
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j) MfmaOp<T>::run(af[s][i], bf[s][j], acc[i][j]);
-            MB_SSTORE((u + 1) % P, (kt + 1) & 1);
-            __syncthreads();
-        }
-    }
-#undef MB_GLOAD
-#undef MB_SSTORE
-    }
-
 
     // ---- epilogue, in FM passes: pass i stages block-row i of every wave (EROWS tile rows)
     //      through LDS. A lane holds column (lane & 31) of each 32x32 block and rows
@@ -839,10 +690,6 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
 }
 
 
-#ifndef MB_GEMM_PREFETCH
-#define MB_GEMM_PREFETCH 2
-#endif
-constexpr int kPrefetch = MB_GEMM_PREFETCH;
 
 // Tile shapes, by grid size (K is 768 or 1152, so a tile lives for only 12-36 K-steps and a
 // small grid is bound by per-workgroup latency and by how evenly the tiles cover 256 CUs):
@@ -855,7 +702,7 @@ template <typename T, int BM, int BN, int NWM, int NWN, int EPI, int OCC, int DS
 int launch_tiles(const GemmArgs& a, hipStream_t s) {
     const int n = ((a.M + BM - 1) / BM) * (a.N / BN);
     if (n == 0) return MBERT_OK;
-    MB_LAUNCH((gemm_kernel<T, BM, BN, NWM, NWN, EPI, kPrefetch, OCC, DS, RB>),
+    MB_LAUNCH((gemm_kernel<T, BM, BN, NWM, NWN, EPI, OCC, DS, RB>),
               xcd_gemm_grid(a.M, BM, a.N, BN), 64 * NWM * NWN, 0, s, a);
     MB_CHECK_LAUNCH();
     return MBERT_OK;
@@ -863,11 +710,11 @@ int launch_tiles(const GemmArgs& a, hipStream_t s) {
 
 template <typename T, int EPI>
 int run_gemm(const GemmArgs& a, hipStream_t s) {
-    if ((a.K * (int)sizeof(T)) % (128 * kPrefetch) != 0) return MBERT_EUNSUPPORTED;
+    if ((a.K * (int)sizeof(T)) % 128 != 0) return MBERT_EUNSUPPORTED;
     const int t128 = ((a.M + 127) / 128) * (a.N / 128);
     const int t256 = ((a.M + 255) / 256) * (a.N / 256);
     if (a.N % 256 == 0 && t256 >= MB_GEMM_BIG_MIN_TILES)
-        return launch_tiles<T, 256, 256, 2, MB_GEMM_BIG_NWN, EPI, 1, MB_GEMM_BIG_DS, MB_GEMM_BIG_RB>(a, s);
+        return launch_tiles<T, 256, 256, 2, 4, EPI, 1, MB_GEMM_BIG_DS, MB_GEMM_BIG_RB>(a, s);
     if (t128 >= MB_GEMM_SMALL_MAX_TILES)
         return launch_tiles<T, 128, 128, 2, 2, EPI, MB_GEMM_MID_OCC, MB_GEMM_MID_DS, MB_GEMM_MID_RB>(a, s);
     if (a.N == D)
@@ -880,7 +727,7 @@ int run_gemm(const GemmArgs& a, hipStream_t s) {
 template <typename T, int EPI>
 int run_gemm_f32(const GemmArgs& a, hipStream_t s) {
     if (a.N % 128 == 0) return run_gemm<T, EPI>(a, s);
-    if ((a.K * (int)sizeof(T)) % (128 * kPrefetch) != 0) return MBERT_EUNSUPPORTED;
+    if ((a.K * (int)sizeof(T)) % 128 != 0) return MBERT_EUNSUPPORTED;
     if (a.M <= 512) return launch_tiles<T, 64, 64, 2, 2, EPI, 4>(a, s);
     return launch_tiles<T, 128, 64, 2, 2, EPI, 3>(a, s);
 }
