@@ -36,11 +36,19 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 template <typename T> struct AttnCfg {
     static constexpr bool F32 = sizeof(T) == 4;
-    static constexpr int KP = F32 ? 68 : 72;   // K row pitch, elements ([key][d])
+    // K row pitch, elements ([key][d]); the 16-bit layout is unpadded (128-byte rows) and
+    // XOR-swizzled by 16-byte chunk (kchunk): conflict-free both for the 16-byte row writes
+    // and for the 16-byte reads of 16 rows at one chunk
+    static constexpr int KP = F32 ? 68 : 64;
     static constexpr int VP = 68;              // V pitch: fp32 [key][d], 16-bit [d][key]
     static constexpr int KSZ = 64 * KP;
     static constexpr int VSZ = 64 * VP;
 };
+
+// Byte offset of 16-byte chunk c (0..7) of K row r in the 16-bit layout: chunk c sits at slot
+// c ^ ((r >> 1) & 7); rows r and r + 1 differ by half of the 256-byte bank window, pairs of
+// rows by the slot.
+__device__ __forceinline__ int kchunk(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
 template <typename T> struct Mma;
 template <> struct Mma<bf16> {
@@ -170,15 +178,18 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
         } else {
 #pragma unroll
             for (int i = 0; i < KCH; ++i)
-                *(u32x4*)(&Ks[st][((tid >> 3) + 32 * i) * C::KP + (tid & 7) * 8]) = rk[u][i];
-            // transpose: Vt[d][key]; one dword holds keys (2kp, 2kp+1) of one d
+                *(u32x4*)(reinterpret_cast<unsigned char*>(&Ks[st][0]) + kchunk((tid >> 3) + 32 * i, tid & 7)) = rk[u][i];
+            // transpose: Vt[d][key]; one dword holds keys (2kp, 2kp+1) of one d. Rows 32-63
+            // store their keys at column key ^ 16 (dword kp ^ 8): without it the lanes writing
+            // rows d and d + 32 of one wave instruction hit the same banks
             const int kp = tid >> 3, d0 = (tid & 7) * 8;
+            const int kps = kp ^ (d0 >= 32 ? 8 : 0);
             unsigned* vt = reinterpret_cast<unsigned*>(&Vs[st][0]);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const unsigned a = rv[u][0][m], b = rv[u][1][m];
-                vt[((d0 + 2 * m) * C::VP) / 2 + kp] = (a & 0xFFFFu) | (b << 16);
-                vt[((d0 + 2 * m + 1) * C::VP) / 2 + kp] = (a >> 16) | (b & 0xFFFF0000u);
+                vt[((d0 + 2 * m) * C::VP) / 2 + kps] = (a & 0xFFFFu) | (b << 16);
+                vt[((d0 + 2 * m + 1) * C::VP) / 2 + kps] = (a >> 16) | (b & 0xFFFF0000u);
             }
         }
     };
@@ -217,7 +228,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
 #pragma unroll
                 for (int c = 0; c < NQ; ++c) {
                     const int d = F32 ? (8 * c + 4 * g) : (16 * c + 8 * g);
-                    const u32x4 a = *(const u32x4*)(&Ks[st][(32 * kk + n) * C::KP + d]);
+                    const u32x4 a = F32 ? *(const u32x4*)(&Ks[st][(32 * kk + n) * C::KP + d])
+                                        : *(const u32x4*)(reinterpret_cast<const unsigned char*>(&Ks[st][0]) +
+                                                          kchunk(32 * kk + n, d / 8));
                     if constexpr (F32) {
                         const f32x4 av = __builtin_bit_cast(f32x4, a), bv = __builtin_bit_cast(f32x4, qf[c]);
 #pragma unroll
@@ -300,7 +313,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
                     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                         for (int h = 0; h < 2; ++h) {
-                            const T* base = &Vs[st][(32 * db + n) * C::VP + 32 * kk + 16 * h + 4 * g];
+                            // rows 32-63 hold their keys at column ^ 16 (see sstore)
+                            const T* base = &Vs[st][(32 * db + n) * C::VP + 32 * kk + 16 * (h ^ db) + 4 * g];
                             const u32x2 lo = *(const u32x2*)base;
                             const u32x2 hi = *(const u32x2*)(base + 8);
                             const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
