@@ -31,8 +31,6 @@
 
 namespace mb {
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 template <typename T> struct AttnCfg {
     static constexpr bool F32 = sizeof(T) == 4;

@@ -86,8 +86,6 @@ namespace mb {
 
 enum { EPI_STORE = 0, EPI_ROPE = 1, EPI_RESID = 2, EPI_GEGLU = 3, EPI_GELU_F32 = 4, EPI_BIAS_F32 = 5 };
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 struct GemmArgs {
     const void* A;       // [M, K] dtype
@@ -263,27 +261,6 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += dpp_f<0x141>(v);  // row_half_mirror
     v += dpp_f<0x140>(v);  // row_mirror
     return v;
-}
-
-__device__ __forceinline__ void buf_store8b(unsigned long long v, const void* base, unsigned extent,
-                                            unsigned off) {
-#if __HIP_DEVICE_COMPILE__
-    __builtin_amdgcn_raw_buffer_store_b64(
-        __builtin_bit_cast(u32x2, v),
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, extent, 0x00020000),
-        off, 0, 0);
-#endif
-}
-
-// 16-byte store through a buffer descriptor (base, extent in bytes): a store at or beyond the
-// extent is dropped by the hardware, so rows past the end need no branch (a branch around a
-// store leaves the compiler unsure how many stores are in flight, and it then waits for all).
-__device__ __forceinline__ void buf_store16(u32x4 v, const void* base, unsigned extent, unsigned off) {
-#if __HIP_DEVICE_COMPILE__
-    __builtin_amdgcn_raw_buffer_store_b128(
-        v, __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, extent, 0x00020000),
-        off, 0, 0);
-#endif
 }
 
 // Eight floats as dtype T to byte offset off of a buffer (16 bytes, or 32 for fp32).
