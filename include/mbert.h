@@ -329,8 +329,12 @@ int mbert_encode_padded_keymask(const mbert_weights* w, const int32_t* ids_pad,
  * stream: group 0 on `stream`, group g on streams[g-1] (n_groups-1 distinct streams, none of
  * them `stream`), forked from `stream` and joined back into it with events, so the call is
  * ordered on `stream` like any other. Sequences never interact, so every output is the
- * same as mbert_encode_padded's; the groups' kernels overlap on the GPU. The workspace holds
- * one region per group: mbert_workspace_bytes_grouped() bytes. n_groups is clamped to B. */
+ * same as mbert_encode_padded's up to rounding; the groups' kernels overlap on the GPU. (The
+ * attention kernel splits each workgroup's key tiles over two wave sets, merging their softmax
+ * states, when its grid has at most 256 workgroups; a group's grid may be below that bound
+ * where the whole batch's is not. Every call with the same groups gives bitwise the same
+ * result.) The workspace holds one region per group: mbert_workspace_bytes_grouped() bytes.
+ * n_groups is clamped to B. */
 size_t mbert_workspace_bytes_grouped(const mbert_config* cfg, mbert_dtype dtype, int B, int Tpad,
                                      int n_groups);
 int mbert_encode_padded_grouped(const mbert_weights* w, const int32_t* ids_pad,

@@ -304,6 +304,35 @@ def test_attention_long_global(dtype):
         assert rel_err(host(o), ref) < TOL_STEP[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("glob", [True, False], ids=["global", "local"])
+def test_attention_split_and_whole_agree(dtype, glob):
+    """A grid of at most one workgroup per CU (256) runs each workgroup's key tiles on two wave
+    sets whose softmax states are merged at the end; a larger grid runs them on one. The same
+    sequences (the edge lengths) through both: once alone (18 tiles x 12 heads = 216 work
+    groups) and three times over (52 x 12 = 624), every copy against the oracle and the two
+    runs against each other."""
+    one = LENGTH_CASES["edges"]
+    cu1, cu3 = cu_from_lengths(one), cu_from_lengths(one * 3)
+    T1, T3 = int(cu1[-1]), int(cu3[-1])
+    grid = lambda T, S: 12 * ((T + 127) // 128 + S)
+    assert grid(T1, len(one)) <= 256 < grid(T3, 3 * len(one))
+    qkv1 = random_matrix((T1, 2304), 93, dtype=dtype, std=1.5)
+    qkv3 = np.concatenate([qkv1] * 3)
+    o1 = torch().full((T1, 768), float("nan"), dtype=_tdt(dtype), device="cuda")
+    o3 = torch().full((T3, 768), float("nan"), dtype=_tdt(dtype), device="cuda")
+    B().mbert_attention(dt(dtype), dev(qkv1, dtype), T1, meta_for(cu1, T1), len(one), glob, 64, o1)
+    B().mbert_attention(dt(dtype), dev(qkv3, dtype), T3, meta_for(cu3, T3), 3 * len(one), glob, 64,
+                        o3)
+    ref = O.attention_varlen(qkv1, O.segments_of(cu1), glob, O.Config())
+    g1, g3 = host(o1), host(o3)
+    assert np.all(np.isfinite(g1)) and np.all(np.isfinite(g3))
+    assert rel_err(g1, ref) < TOL_STEP[dtype]
+    for c in range(3):
+        assert rel_err(g3[c * T1:(c + 1) * T1], ref) < TOL_STEP[dtype]
+        assert rel_err(g3[c * T1:(c + 1) * T1], g1) < TOL_STEP[dtype]
+
+
 # ---------------------------------------------------------------------------- final LN + pool
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("case", ["edges", "one1000"])

@@ -6,9 +6,12 @@
 //
 // Work: one workgroup per (work tile of <= 128 query rows of one sequence, head); 4 wave64s,
 // 32 query rows each. K/V tiles of 64 keys stream through two LDS stages (prefetched into
-// registers one tile ahead, with unconditional loads). The workgroup walks only the keys its band can reach: the whole
-// sequence on a global layer, [q0 - W, q0 + qn - 1 + W] on a local one; a wave whose own
-// band misses a key tile skips its MFMAs for it.
+// registers one tile ahead, with unconditional loads). The workgroup walks only the keys its
+// band can reach: the whole sequence on a global layer, [q0 - W, q0 + qn - 1 + W] on a local
+// one; a wave whose own band misses a key tile skips its MFMAs for it. On a grid of at most
+// one workgroup per CU (16-bit types), the workgroup has 8 waves: the second four take the
+// odd key tiles, two tiles are staged per step, and the two online-softmax states of each
+// query are merged at the end (the usual rescale-and-add of partial softmax sums).
 //
 // Layout trick: each wave computes S^T = K Q^T (32x32 MFMA blocks: rows = keys,
 // columns = queries), so every lane owns one query column: the row max, row sum and the
@@ -28,8 +31,16 @@
 #ifndef MB_ATTN_PREFETCH
 #define MB_ATTN_PREFETCH 1
 #endif
+// Largest grid ((work tile, head) pairs) run with the key tiles split over two wave sets: one
+// workgroup per CU at most. Beyond that some CUs hold two 8-wave workgroups and set the pace
+// (a 2445-token batch in 264 workgroups: global layer 16.1 -> 17.2 us, while 132 workgroups
+// of half of it gain 12.7 -> 11.1 us).
+#ifndef MB_ATTN_SPLIT_MAX_WG
+#define MB_ATTN_SPLIT_MAX_WG 256
+#endif
 
 namespace mb {
+constexpr int ATTN_SPLIT_MAX_WG = MB_ATTN_SPLIT_MAX_WG;
 
 
 template <typename T> struct AttnCfg {
@@ -72,15 +83,17 @@ template <> struct Mma<f16> {
     }
 };
 
-template <typename T>
-__global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv, T* __restrict__ out,
+template <typename T, int KS>
+__global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(const T* __restrict__ qkv, T* __restrict__ out,
                                                       const int* __restrict__ meta, int total_max,
                                                       int S, int tiles_max, int is_global, int W,
                                                       float scale_log2) {
     using C = AttnCfg<T>;
     constexpr bool F32 = C::F32;
-    __shared__ __align__(16) T Ks[2][C::KSZ];
-    __shared__ __align__(16) T Vs[2][C::VSZ];
+    static_assert(KS == 1 || (KS == 2 && !F32), "key halves for the 16-bit types");
+    // [stage][key half]: with KS = 2 the workgroup stages two key tiles per step, one per half
+    __shared__ __align__(16) T Ks[2][KS][C::KSZ];
+    __shared__ __align__(16) T Vs[2][KS][C::VSZ];
 
     const MetaView mv = meta_view(const_cast<int*>(meta), total_max, S);
     // (head, tile) pairs of the real tile count, spread over the XCDs in contiguous ranges:
@@ -96,10 +109,14 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
     const int4 tl = mv.tiles[tile];
     const int q0 = tl.x, qn = tl.y, s0 = tl.z, s1 = tl.w;
 
+    // wave w: queries 32 (w % 4) .. +31 of the tile, key tiles kh, kh + KS, kh + 2 KS, ...
+    // (kh = w / 4); staging thread tid loads key tile KS i + sh of step i (sh = tid / 256)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int qg = wave & 3, kh = wave >> 2;
+    const int stid = tid & 255, sh = tid >> 8;
     const int n = lane & 31, g = lane >> 5;
-    const int qw0 = q0 + 32 * wave;
-    const int qcnt = min(32, qn - 32 * wave);
+    const int qw0 = q0 + 32 * qg;
+    const int qcnt = min(32, qn - 32 * qg);
 
     int klo, khi, tmp;
     key_range(q0, s0, s1, is_global, W, klo, tmp);
@@ -115,7 +132,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
     const int nkt = (khi - klo) / 64 + 1;
 
     // this lane's query (loads clamped into the tile) and its band
-    const int qrow = q0 + min(32 * wave + n, qn - 1);
+    const int qrow = q0 + min(32 * qg + n, qn - 1);
     int qlo, qhi;
     key_range(qw0 + n, s0, s1, is_global, W, qlo, qhi);
     // keys valid for every query of the wave: [lo of the last query, hi of the first]
@@ -141,8 +158,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
     constexpr int KCH = F32 ? 4 : 2;  // 16-byte chunks per thread for K (and V for fp32)
     constexpr int AP = MB_ATTN_PREFETCH;  // K/V tiles held in registers ahead of the LDS stage
     u32x4 rk[AP][KCH], rv[AP][KCH];
-    auto gload = [&](int it, int u) {
-        const int kb = klo + 64 * it;
+    auto gload = [&](int step, int u) {
+        const int kb = klo + 64 * min(KS * step + sh, nkt - 1);
         if constexpr (F32) {
 #pragma unroll
             for (int i = 0; i < KCH; ++i) {
@@ -154,14 +171,14 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
         } else {
 #pragma unroll
             for (int i = 0; i < KCH; ++i) {
-                const int key = min(kb + (tid >> 3) + 32 * i, khi);
-                rk[u][i] = *(const u32x4*)(qkv + (size_t)key * QKV + D + head * HD + (tid & 7) * 8);
+                const int key = min(kb + (stid >> 3) + 32 * i, khi);
+                rk[u][i] = *(const u32x4*)(qkv + (size_t)key * QKV + D + head * HD + (stid & 7) * 8);
             }
-            const int kp = tid >> 3;  // key pair
+            const int kp = stid >> 3;  // key pair
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int key = min(kb + 2 * kp + i, khi);
-                rv[u][i] = *(const u32x4*)(qkv + (size_t)key * QKV + 2 * D + head * HD + (tid & 7) * 8);
+                rv[u][i] = *(const u32x4*)(qkv + (size_t)key * QKV + 2 * D + head * HD + (stid & 7) * 8);
             }
         }
     };
@@ -170,19 +187,19 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
 #pragma unroll
             for (int i = 0; i < KCH; ++i) {
                 const int off = ((tid >> 4) + 16 * i) * C::KP + (tid & 15) * 4;
-                *(u32x4*)(&Ks[st][off]) = rk[u][i];
-                *(u32x4*)(&Vs[st][off]) = rv[u][i];
+                *(u32x4*)(&Ks[st][sh][off]) = rk[u][i];
+                *(u32x4*)(&Vs[st][sh][off]) = rv[u][i];
             }
         } else {
 #pragma unroll
             for (int i = 0; i < KCH; ++i)
-                *(u32x4*)(reinterpret_cast<unsigned char*>(&Ks[st][0]) + kchunk((tid >> 3) + 32 * i, tid & 7)) = rk[u][i];
+                *(u32x4*)(reinterpret_cast<unsigned char*>(&Ks[st][sh][0]) + kchunk((stid >> 3) + 32 * i, stid & 7)) = rk[u][i];
             // transpose: Vt[d][key]; one dword holds keys (2kp, 2kp+1) of one d. Rows 32-63
             // store their keys at column key ^ 16 (dword kp ^ 8): without it the lanes writing
             // rows d and d + 32 of one wave instruction hit the same banks
-            const int kp = tid >> 3, d0 = (tid & 7) * 8;
+            const int kp = stid >> 3, d0 = (stid & 7) * 8;
             const int kps = kp ^ (d0 >= 32 ? 8 : 0);
-            unsigned* vt = reinterpret_cast<unsigned*>(&Vs[st][0]);
+            unsigned* vt = reinterpret_cast<unsigned*>(&Vs[st][sh][0]);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const unsigned a = rv[u][0][m], b = rv[u][1][m];
@@ -201,20 +218,22 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
     float m_run = -INFINITY, l_run = 0.f;
 
     // Every load is unconditional (a tile past the last re-reads the last one): loads under a
-    // branch leave the wait-count pass unsure of what is in flight. Tile t is held in
-    // register slot t % AP; the loop is unrolled AP times so the slots are static.
+    // branch leave the wait-count pass unsure of what is in flight. Step i's tiles are held in
+    // register slot i % AP; the loop is unrolled AP times so the slots are static.
+    const int nst = (nkt + KS - 1) / KS;  // steps of KS key tiles
 #pragma unroll
-    for (int u = 0; u < AP; ++u) gload(min(u, nkt - 1), u);
+    for (int u = 0; u < AP; ++u) gload(u, u);
     sstore(0, 0);
     __syncthreads();
-    for (int it0 = 0; it0 < nkt; it0 += AP) {
+    for (int it0 = 0; it0 < nst; it0 += AP) {
 #pragma unroll
     for (int u = 0; u < AP; ++u) {
         const int it = it0 + u;
-        if (it >= nkt) break;  // uniform over the workgroup
-        gload(min(it + AP, nkt - 1), u);
-        const int kb = klo + 64 * it;
-        const bool active = qcnt > 0 && kb <= whi && kb + 63 >= wlo;
+        if (it >= nst) break;  // uniform over the workgroup
+        gload(it + AP, u);
+        const int t = KS * it + kh;  // this wave's key tile
+        const int kb = klo + 64 * t;
+        const bool active = t < nkt && qcnt > 0 && kb <= whi && kb + 63 >= wlo;
         if (active) {
             const int st = it & 1;
             // ---- S^T = K Q^T for keys kb .. kb+63 (two 32-key blocks)
@@ -226,8 +245,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
 #pragma unroll
                 for (int c = 0; c < NQ; ++c) {
                     const int d = F32 ? (8 * c + 4 * g) : (16 * c + 8 * g);
-                    const u32x4 a = F32 ? *(const u32x4*)(&Ks[st][(32 * kk + n) * C::KP + d])
-                                        : *(const u32x4*)(reinterpret_cast<const unsigned char*>(&Ks[st][0]) +
+                    const u32x4 a = F32 ? *(const u32x4*)(&Ks[st][kh][(32 * kk + n) * C::KP + d])
+                                        : *(const u32x4*)(reinterpret_cast<const unsigned char*>(&Ks[st][kh][0]) +
                                                           kchunk(32 * kk + n, d / 8));
                     if constexpr (F32) {
                         const f32x4 av = __builtin_bit_cast(f32x4, a), bv = __builtin_bit_cast(f32x4, qf[c]);
@@ -296,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
 #pragma unroll
                         for (int e = 0; e < 16; ++e) {
                             const int key = 32 * kk + 8 * (e >> 2) + 4 * g + (e & 3);
-                            const float a = Vs[st][key * C::VP + 32 * db + n];
+                            const float a = Vs[st][kh][key * C::VP + 32 * db + n];
                             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, sv[16 * kk + e], oacc[db], 0, 0, 0);
                         }
             } else {
@@ -312,7 +331,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
 #pragma unroll
                         for (int h = 0; h < 2; ++h) {
                             // rows 32-63 hold their keys at column ^ 16 (see sstore)
-                            const T* base = &Vs[st][(32 * db + n) * C::VP + 32 * kk + 16 * (h ^ db) + 4 * g];
+                            const T* base = &Vs[st][kh][(32 * db + n) * C::VP + 32 * kk + 16 * (h ^ db) + 4 * g];
                             const u32x2 lo = *(const u32x2*)base;
                             const u32x2 hi = *(const u32x2*)(base + 8);
                             const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
@@ -320,9 +339,37 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const T* __restrict__ qkv,
                         }
             }
         }
-        if (it + 1 < nkt) sstore((it + 1) & 1, (u + 1) % AP);
+        if (it + 1 < nst) sstore((it + 1) & 1, (u + 1) % AP);
         __syncthreads();
     }
+    }
+
+    if constexpr (KS == 2) {
+        // Merge the key halves (every wave is past the loop's last barrier, so the V stages
+        // are free): waves 4-7 leave their running max, sum and output in LDS, waves 0-3 add
+        // them in on the larger of the two maxima. A half that saw no key has max -inf and
+        // weight 0.
+        float* xm = reinterpret_cast<float*>(&Vs[0][0][0]) + qg * 34 * 64 + lane;
+        static_assert(sizeof(Vs) >= 4 * 34 * 64 * sizeof(float), "merge area");
+        if (kh == 1) {
+            xm[0] = m_run;
+            xm[64] = l_run;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) xm[(2 + 16 * db + e) * 64] = oacc[db][e];
+        }
+        __syncthreads();
+        if (kh == 1) return;
+        const float m1 = xm[0], l1 = xm[64];
+        const float mm = fmaxf(m_run, m1);
+        const float f0 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+        const float f1 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+        l_run = l_run * f0 + l1 * f1;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[db][e] = oacc[db][e] * f0 + xm[(2 + 16 * db + e) * 64] * f1;
     }
 
     // ---- normalise and write: lane holds d = 32 db + 8 j + 4 g + i of its query
@@ -409,18 +456,30 @@ int launch_attention(mbert_dtype dt, const void* qkv, int total, const int32_t* 
     if (tmax == 0) return MBERT_OK;
     const unsigned grid = (unsigned)xcd_grid(NH * tmax);
     const float scale_log2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
+    // A grid of at most one workgroup per CU leaves most SIMDs with one wave or none: then
+    // each workgroup splits its key tiles over two sets of four waves, which halves the chain
+    // of tiles a wave walks (the sets merge their softmax states at the end).
+    const bool split = NH * tmax <= ATTN_SPLIT_MAX_WG;
     switch (dt) {
         case MBERT_F32:
-            MB_LAUNCH((attn_kernel<float>), grid, 256, 0, s, (const float*)qkv, (float*)o, meta, total, n_seqs,
-                                                    tmax, is_global, W, scale_log2);
+            MB_LAUNCH((attn_kernel<float, 1>), grid, 256, 0, s, (const float*)qkv, (float*)o, meta, total,
+                      n_seqs, tmax, is_global, W, scale_log2);
             break;
         case MBERT_BF16:
-            MB_LAUNCH((attn_kernel<bf16>), grid, 256, 0, s, (const bf16*)qkv, (bf16*)o, meta, total, n_seqs,
-                                                   tmax, is_global, W, scale_log2);
+            if (split)
+                MB_LAUNCH((attn_kernel<bf16, 2>), grid, 512, 0, s, (const bf16*)qkv, (bf16*)o, meta, total,
+                          n_seqs, tmax, is_global, W, scale_log2);
+            else
+                MB_LAUNCH((attn_kernel<bf16, 1>), grid, 256, 0, s, (const bf16*)qkv, (bf16*)o, meta, total,
+                          n_seqs, tmax, is_global, W, scale_log2);
             break;
         case MBERT_F16:
-            MB_LAUNCH((attn_kernel<f16>), grid, 256, 0, s, (const f16*)qkv, (f16*)o, meta, total, n_seqs,
-                                                  tmax, is_global, W, scale_log2);
+            if (split)
+                MB_LAUNCH((attn_kernel<f16, 2>), grid, 512, 0, s, (const f16*)qkv, (f16*)o, meta, total,
+                          n_seqs, tmax, is_global, W, scale_log2);
+            else
+                MB_LAUNCH((attn_kernel<f16, 1>), grid, 256, 0, s, (const f16*)qkv, (f16*)o, meta, total,
+                          n_seqs, tmax, is_global, W, scale_log2);
             break;
         default:
             return MBERT_EUNSUPPORTED;
