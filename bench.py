@@ -517,10 +517,15 @@ def main():
 
     heads = None
     if not args.no_heads:
-        # the last eager forward's packed rows: the workspace's out region (padded batch) or
-        # the caller's out (packed batch)
+        # the last eager forward's rows, packed (input set-up for the head timings: the real
+        # rows of the padded output gathered in order, or the packed batch's output as is)
         total_max = Bn * Tp if padded else T
-        rows_ptr = ws.data_ptr() + m.layout(total_max, S).out if padded else out.data_ptr()
+        if padded:
+            packed_rows = torch.zeros((total_max, 768), dtype=torch.float32, device=dev)
+            packed_rows[:T] = out.view(-1, 768)[torch.from_numpy(batch["mask"].astype(bool).ravel()).to(dev)]
+            rows_ptr = packed_rows.data_ptr()
+        else:
+            rows_ptr = out.data_ptr()
         heads = measure_heads(B, m, wl, ws, rows_ptr, total_max, T, S, stream,
                               min(args.steps, 20))
 

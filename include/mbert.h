@@ -281,10 +281,11 @@ int mbert_repad(const float* out, const int32_t* rowmap, int B, int Tpad, float*
  * Device scratch for one forward; the caller allocates mbert_workspace_bytes() bytes
  * (256-byte aligned). Layout (byte offsets from mbert_workspace_layout): resid f32
  * [Tmax,768], h dtype [Tmax,768] (also the attention output), qkv dtype [Tmax,2304] (also the
- * GeGLU output), meta, pool partials, for the padded path ids/indices/rowmap/cu/out, and for
- * folded LayerNorms xs dtype [Tmax,768] (the residual rounded) and rstats f32 [Tmax,12,2]. */
+ * GeGLU output), meta, pool partials, for the padded path ids/indices/rowmap/cu, and for
+ * folded LayerNorms xs dtype [Tmax,768] (the residual rounded) and rstats f32 [Tmax,12,2].
+ * (The padded path's final norm writes the caller's padded output directly.) */
 typedef struct {
-    size_t resid, h, qkv, meta, partials, ids, indices, rowmap, cu, out, xs, rstats, total_bytes;
+    size_t resid, h, qkv, meta, partials, ids, indices, rowmap, cu, xs, rstats, total_bytes;
 } mbert_ws_layout;
 size_t mbert_workspace_bytes(const mbert_config* cfg, mbert_dtype dtype, int total_max,
                              int n_seqs);

@@ -111,6 +111,39 @@ def test_unpad_edges_and_holes():
     assert meta[3] & B().STATUS_BAD_MASK
 
 
+@pytest.mark.parametrize("shape", [(4, 4096), (5, 4000), (1, 16385), (3, 1)],
+                         ids=["16384-one-workgroup", "20000-three-kernels", "16385", "3x1"])
+def test_unpad_both_paths_bit_exact(shape):
+    """Up to 16,384 slots the unpadding runs as one workgroup (one scan pass over the slots),
+    beyond as three kernels (count, scan, compact); random masks with holes, an empty row and a
+    full row, against the oracle bit for bit, then a row over max_positions and a mask value
+    of 2 flagging their status bits the same way."""
+    g = np.random.default_rng(shape[0] * 100003 + shape[1])
+    mask = (g.random(shape) < 0.6).astype(np.int64)
+    mask[0] = 1
+    if shape[0] > 2:
+        mask[1] = 0
+    ids_pad = g.integers(0, 50368, size=shape)
+    ref = O.unpad(ids_pad, mask)
+    got, cu, meta = _unpad_gpu(ids_pad, mask, max_pos=max(8192, shape[1]))
+    T, Bn = len(ref["ids"]), shape[0]
+    counts, pos, first, tiles = split_meta(meta, mask.size, Bn)
+    assert list(counts[:4]) == [T, ref["max_seqlen"], len(expected_tiles(ref["cu_seqlens"], 128)[0]), 0]
+    assert np.array_equal(cu, ref["cu_seqlens"])
+    assert np.array_equal(got["ids"][:T], ref["ids"]) and np.array_equal(pos[:T], ref["pos"])
+    assert np.array_equal(got["indices"][:T], ref["indices"])
+    rowmap = np.full(mask.size, -1)
+    rowmap[ref["indices"]] = np.arange(T)
+    assert np.array_equal(got["rowmap"], rowmap)
+    assert np.array_equal(tiles, expected_tiles(ref["cu_seqlens"], 128)[0])
+    if ref["max_seqlen"] > 1:
+        _, _, meta = _unpad_gpu(ids_pad, mask, max_pos=int(ref["max_seqlen"]) - 1)
+        assert meta[3] & B().STATUS_TOO_LONG
+    mask[-1, -1] = 2
+    _, _, meta = _unpad_gpu(ids_pad, mask, max_pos=max(8192, shape[1]))
+    assert meta[3] & B().STATUS_BAD_MASK and not meta[3] & B().STATUS_TOO_LONG
+
+
 @pytest.mark.parametrize("case", list(LENGTH_CASES) + ["c4"])
 @pytest.mark.parametrize("W", [64, 3, 0])
 def test_key_ranges_bit_exact(case, W):

@@ -81,12 +81,12 @@ def test_meta_and_workspace_layout():
         off = 8 + T + S + 1
         off = (off + 3) & ~3
         assert B.mbert_meta_ints(T, S) == off + 4 * tiles_max
-        assert B.mbert_pool_partial_floats(T, S) == tiles_max * 768
+        assert B.mbert_pool_partial_floats(T, S) == tiles_max * 4 * 768  # 4 partials per tile
         for dt, ds in ((B.MBERT_F32, 4), (B.MBERT_BF16, 2), (B.MBERT_F16, 2)):
             L = B.mbert_workspace_layout(c, dt, T, S)
-            offs = [L.resid, L.h, L.qkv, L.meta, L.partials, L.ids, L.indices, L.rowmap, L.cu, L.out]
+            offs = [L.resid, L.h, L.qkv, L.meta, L.partials, L.ids, L.indices, L.rowmap, L.cu]
             sizes = [T * 768 * 4, T * 768 * ds, T * 2304 * ds, 4 * B.mbert_meta_ints(T, S),
-                     4 * tiles_max * 768, 4 * T, 4 * T, 4 * T, 4 * (S + 1), T * 768 * 4]
+                     4 * tiles_max * 4 * 768, 4 * T, 4 * T, 4 * T, 4 * (S + 1)]
             assert all(o % 256 == 0 for o in offs)
             for o, s, nxt in zip(offs, sizes, offs[1:] + [L.total_bytes]):
                 assert o + s <= nxt

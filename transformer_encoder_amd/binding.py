@@ -53,7 +53,7 @@ class mbert_weights(Structure):
 
 class mbert_ws_layout(Structure):
     _fields_ = [(n, c_size_t) for n in ("resid", "h", "qkv", "meta", "partials", "ids", "indices",
-                                        "rowmap", "cu", "out", "xs", "rstats",
+                                        "rowmap", "cu", "xs", "rstats",
                                         "total_bytes")]
 
 

@@ -73,12 +73,11 @@ mbert_ws_layout make_layout(mbert_dtype dt, int total_max, int n_seqs) {
     L.h = take(T * D * ds);
     L.qkv = take(T * QKV * ds);
     L.meta = take(meta_ints(total_max, n_seqs) * 4);
-    L.partials = take(tiles_max_for(total_max, n_seqs) * D * 4);
+    L.partials = take(tiles_max_for(total_max, n_seqs) * FPARTS * D * 4);
     L.ids = take(T * 4);
     L.indices = take(T * 4);
     L.rowmap = take(T * 4);
     L.cu = take(((size_t)n_seqs + 1) * 4);
-    L.out = take(T * D * 4);
     L.xs = take(T * D * ds);
     L.rstats = take(T * 12 * 8);
     L.total_bytes = off;
@@ -307,7 +306,6 @@ int encode_padded_impl(const mbert_weights* w, const int32_t* ids_pad, const int
     int32_t* meta = reinterpret_cast<int32_t*>(base + L.meta);
     int32_t* ids = reinterpret_cast<int32_t*>(base + L.ids);
     float* resid = reinterpret_cast<float*>(base + L.resid);
-    float* out = reinterpret_cast<float*>(base + L.out);
     MB_TIMED(rec, MBERT_K_META, s,
              mbh::launch_unpad(ids_pad, mask, B, Tpad, w->cfg.max_positions, ids,
                                reinterpret_cast<int32_t*>(base + L.indices),
@@ -320,11 +318,13 @@ int encode_padded_impl(const mbert_weights* w, const int32_t* ids_pad, const int
         for (int l = 0; l < w->cfg.n_layers; ++l)
             MB_TRY(run_layer(w, l, total_max, B, base, L, s, rec, use_fold(w)));
     }
+    // the final norm writes the padded output directly (rows by their slot; pads zeroed)
     MB_TIMED(rec, MBERT_K_FINAL_POOL, s,
              mbh::launch_final_ln_pool(resid, total_max, meta, B, w->dtype, w->final_norm,
-                                       w->cfg.norm_eps, out, pooled,
-                                       reinterpret_cast<float*>(base + L.partials), s));
-    MB_TRY(mbh::launch_repad(out, reinterpret_cast<int32_t*>(base + L.rowmap), B, Tpad, out_pad, s));
+                                       w->cfg.norm_eps, out_pad, pooled,
+                                       reinterpret_cast<float*>(base + L.partials), s,
+                                       reinterpret_cast<int32_t*>(base + L.indices),
+                                       reinterpret_cast<int32_t*>(base + L.rowmap), total_max));
     return MBERT_OK;
 }
 
@@ -546,7 +546,7 @@ int mbert_mlp_in_geglu(mbert_dtype dt, const void* h, int total, const int32_t* 
 
 size_t mbert_pool_partial_floats(int total_max, int n_seqs) {
     if (total_max < 0 || n_seqs < 0) return 0;
-    return tiles_max_for(total_max, n_seqs) * D;
+    return tiles_max_for(total_max, n_seqs) * FPARTS * D;
 }
 
 int mbert_final_ln_pool(const float* resid, int total, const int32_t* meta, int n_seqs,

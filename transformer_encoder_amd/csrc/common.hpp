@@ -17,6 +17,7 @@ constexpr int HD = 64;        // head width
 constexpr int FF = 1152;      // GeGLU intermediate width
 constexpr int QKV = 3 * D;    // fused projection width
 constexpr int TILE = 128;     // query rows per attention / pooling work tile
+constexpr int FPARTS = 4;     // pooling partial sums per work tile (one per 32 rows)
 constexpr int NXCD = 8;       // accelerator complex dies on MI355X
 
 typedef __bf16 bf16;
@@ -206,9 +207,13 @@ int launch_padded_meta(const int32_t* mask, int B, int Tpad, int max_pos, int32_
                        hipStream_t s);
 int launch_attention_probs(mbert_dtype dt, const void* qkv, int row0, int n_q, int n_k,
                            int is_global, int W, float* probs, hipStream_t s);
+// Final LayerNorm (+ pooling partials and mean pooling when pooled != NULL). With `scatter`,
+// packed row k goes to row scatter[k] of `out` and the n_slots rows whose rowmap entry is
+// negative are zeroed in the same launch (the padded output written directly).
 int launch_final_ln_pool(const float* resid, int total, const int32_t* meta, int n_seqs,
                          mbert_dtype dt, const void* w, float eps, float* out, float* pooled,
-                         float* partials, hipStream_t s);
+                         float* partials, hipStream_t s, const int32_t* scatter = nullptr,
+                         const int32_t* rowmap = nullptr, int n_slots = 0);
 // A LayerNorm folded into the GEMM that follows it: the A operand is the raw residual (in
 // dtype; the fp32 residual itself for MBERT_F32), W is the folded weight (W o w), and the
 // epilogue applies rstd * (acc - mean * c) from the producer's chunk statistics.

@@ -284,6 +284,94 @@ __global__ __launch_bounds__(256) void unpad_compact_kernel(const int* __restric
     }
 }
 
+// Padded path in one workgroup (small batches): the three steps above in a single launch. One
+// pass over the B x Tpad slots in row-major chunks of 1024: a block-wide exclusive scan of the
+// real-token flags gives each real slot its packed row k (tokens are packed row by row, so k
+// counts the real slots before it), the first slot of row b records cu[b], and the position is
+// k - cu[b]. All mask and id loads are issued before the first scan.
+constexpr int UNPAD_FUSED_CHUNKS = 16;  // slots per thread: up to 16 x 1024 slots
+__global__ __launch_bounds__(1024) void unpad_fused_kernel(const int* __restrict__ ids_pad,
+                                                           const int* __restrict__ mask, int B,
+                                                           int Tpad, int max_pos,
+                                                           int* __restrict__ ids,
+                                                           int* __restrict__ indices,
+                                                           int* __restrict__ rowmap,
+                                                           int* __restrict__ cu,
+                                                           int* __restrict__ meta, int total_max) {
+    __shared__ int lds[32];
+    __shared__ int s_status, s_maxlen;
+    const MetaView mv = meta_view(meta, total_max, B);
+    const int n = B * Tpad, tid = threadIdx.x;
+    if (tid == 0) {
+        s_status = 0;
+        s_maxlen = 0;
+    }
+    int mv_[UNPAD_FUSED_CHUNKS] = {}, idv[UNPAD_FUSED_CHUNKS] = {};
+    if (n > 0) {
+#pragma unroll
+        for (int c = 0; c < UNPAD_FUSED_CHUNKS; ++c) {
+            const int slot = min(c * 1024 + tid, n - 1);  // past the end: re-read the last slot
+            mv_[c] = mask[slot];
+            idv[c] = ids_pad[slot];
+        }
+    }
+    if (Tpad == 0)
+        for (int b = tid; b <= B; b += blockDim.x) cu[b] = 0;
+    __syncthreads();
+    int carry = 0, bad = 0;
+#pragma unroll
+    for (int c = 0; c < UNPAD_FUSED_CHUNKS; ++c) {
+        if (c * 1024 >= n) break;  // uniform
+        const int slot = c * 1024 + tid;
+        const bool in = slot < n;
+        const int real = in && mv_[c] != 0;
+        bad |= in && mv_[c] != 0 && mv_[c] != 1;
+        int tot;
+        const int k = carry + block_excl_scan(real, lds, tot);
+        const int b = in ? slot / Tpad : 0;
+        if (in && slot == b * Tpad) cu[b] = k;
+        if (in) {
+            rowmap[slot] = real ? k : -1;
+            if (real) {
+                ids[k] = idv[c];
+                indices[k] = slot;
+            }
+        }
+        carry += tot;
+    }
+    if (tid == 0 && Tpad > 0) cu[B] = carry;
+    __syncthreads();  // every cu entry written
+    // positions: rank among the row's real tokens
+#pragma unroll
+    for (int c = 0; c < UNPAD_FUSED_CHUNKS; ++c) {
+        const int slot = c * 1024 + tid;
+        if (c * 1024 >= n) break;
+        if (slot < n && mv_[c] != 0) {
+            const int b = slot / Tpad;
+            const int k = rowmap[slot];
+            mv.pos[k] = k - cu[b];
+        }
+    }
+    int status = bad ? MBERT_STATUS_BAD_MASK : 0, maxlen = 0;
+    for (int b = tid; b < B; b += blockDim.x) {
+        const int L = cu[b + 1] - cu[b];
+        if (L > max_pos) status |= MBERT_STATUS_TOO_LONG;
+        maxlen = max(maxlen, L);
+    }
+    if (status) atomicOr(&s_status, status);
+    atomicMax(&s_maxlen, maxlen);
+    __syncthreads();
+    status = s_status;
+    const bool ok = (status & MBERT_STATUS_TOO_LONG) == 0;
+    build_tiles(cu, B, ok, mv, lds);
+    if (tid == 0) {
+        mv.counts[MBERT_META_TOTAL] = carry;
+        mv.counts[MBERT_META_MAXLEN] = ok ? s_maxlen : 0;
+        mv.counts[MBERT_META_STATUS] = status;
+        for (int i = 4; i < 8; ++i) mv.counts[i] = 0;
+    }
+}
+
 // Per-token key ranges through the attention kernel's own band function.
 __global__ __launch_bounds__(TILE) void key_range_kernel(const int* __restrict__ meta, int total_max,
                                                          int S, int is_global, int W,
@@ -358,6 +446,12 @@ int launch_unpad(const int32_t* ids_pad, const int32_t* mask, int B, int Tpad, i
                  int32_t* ids, int32_t* indices, int32_t* rowmap, int32_t* cu, int32_t* meta,
                  hipStream_t s) {
     const int total_max = B * Tpad;
+    if ((long)B * Tpad <= 1024L * UNPAD_FUSED_CHUNKS) {
+        MB_LAUNCH((unpad_fused_kernel), 1, 1024, 0, s, ids_pad, mask, B, Tpad, max_pos, ids, indices, rowmap,
+                  cu, meta, total_max);
+        MB_CHECK_LAUNCH();
+        return MBERT_OK;
+    }
     if (B > 0) {
         MB_LAUNCH((unpad_count_kernel), B, 256, 0, s, mask, Tpad, cu);
         MB_CHECK_LAUNCH();

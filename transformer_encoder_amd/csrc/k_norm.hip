@@ -84,10 +84,18 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
     store_row12(y + row * D, lane, v);
 }
 
-// Final LayerNorm over one work tile (<= 128 rows of one sequence) plus the tile's column sums
-// of the normalised rows, reduced in a fixed order (no atomics: bitwise reproducible). Sixteen
-// waves per tile keep eight rows in flight per wave.
-constexpr int FWAVES = 16;
+// Final LayerNorm plus pooling partial sums. Work unit: one quarter of a work tile (<= 32 rows
+// of one sequence), 4 waves of 8 rows each, all 8 rows' loads in flight before any is
+// normalised; the unit's column sums of its normalised rows are reduced over the waves in a
+// fixed order into partials[(tile * FPARTS + quarter) * 768] (no atomics: bitwise
+// reproducible). Rows at or past the sequence's key end (the pad rows of a padded batch run at
+// full width) are written as zeros and left out of the sums.
+// With `scatter`, packed row k is written to row scatter[k] of `out` (the padded output), and
+// the workgroups after the LayerNorm ones write zeros to every row whose rowmap entry is
+// negative (the pads): the re-pad is part of this launch.
+constexpr int FROWS = TILE / FPARTS;    // rows per workgroup
+constexpr int FWAVES = 4;
+constexpr int FRW = FROWS / FWAVES;     // rows per wave
 
 template <typename T>
 __global__ __launch_bounds__(64 * FWAVES) void final_ln_kernel(const float* __restrict__ resid,
@@ -95,41 +103,52 @@ __global__ __launch_bounds__(64 * FWAVES) void final_ln_kernel(const float* __re
                                                                int total_max, int S,
                                                                const T* __restrict__ w, float eps,
                                                                float* __restrict__ out,
-                                                               float* __restrict__ partials) {
+                                                               float* __restrict__ partials,
+                                                               int ln_blocks,
+                                                               const int* __restrict__ scatter,
+                                                               const int* __restrict__ rowmap,
+                                                               int n_slots) {
     __shared__ float red[FWAVES][D];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if ((int)blockIdx.x >= ln_blocks) {  // pad rows of the padded output
+        const float z[12] = {};
+        const int stride = (gridDim.x - ln_blocks) * FWAVES;
+        for (int r = ((int)blockIdx.x - ln_blocks) * FWAVES + wave; r < n_slots; r += stride)
+            if (rowmap[r] < 0) store_row12(out + (long)r * D, lane, z);
+        return;
+    }
     const MetaView mv = meta_view(const_cast<int*>(meta), total_max, S);
-    const int b = blockIdx.x;
+    const int b = blockIdx.x / FPARTS, q = blockIdx.x % FPARTS;
     if (b >= mv.counts[MBERT_META_NTILES]) return;
     const int4 tl = mv.tiles[b];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r0 = q * FROWS;
+    if (r0 >= tl.y) {  // an empty quarter still leaves its (zero) partial sums
+        if (partials)
+            for (int col = threadIdx.x; col < D; col += 64 * FWAVES) partials[(long)blockIdx.x * D + col] = 0.f;
+        return;
+    }
+    const int real = min(tl.y, tl.w - tl.x);
+    float v[FRW][12];
+#pragma unroll
+    for (int k = 0; k < FRW; ++k)
+        load_row12(resid + (long)(tl.x + min(r0 + wave + FWAVES * k, tl.y - 1)) * D, lane, v[k]);
     float acc[12];
 #pragma unroll
     for (int i = 0; i < 12; ++i) acc[i] = 0.f;
-    // a wave takes rows wave, wave + 16, ... four at a time: the four loads are in flight
-    // together (a row past the tile re-reads the tile's last row and is dropped). Rows at or
-    // past the sequence's key end (the pad rows of a padded batch run at full width) are
-    // written as zeros and left out of the pooling sums.
-    constexpr int RB = 4;
-    const int real = min(tl.y, tl.w - tl.x);
-    for (int r0 = wave; r0 < tl.y; r0 += RB * FWAVES) {
-        float v[RB][12];
 #pragma unroll
-        for (int k = 0; k < RB; ++k)
-            load_row12(resid + (long)(tl.x + min(r0 + FWAVES * k, tl.y - 1)) * D, lane, v[k]);
+    for (int k = 0; k < FRW; ++k) {
+        const int r = r0 + wave + FWAVES * k;
+        if (r >= tl.y) break;
+        if (r < real) {
+            layernorm12(v[k], w, lane, eps);
 #pragma unroll
-        for (int k = 0; k < RB; ++k) {
-            const int r = r0 + FWAVES * k;
-            if (r >= tl.y) break;
-            if (r < real) {
-                layernorm12(v[k], w, lane, eps);
+            for (int i = 0; i < 12; ++i) acc[i] += v[k][i];
+        } else {
 #pragma unroll
-                for (int i = 0; i < 12; ++i) acc[i] += v[k][i];
-            } else {
-#pragma unroll
-                for (int i = 0; i < 12; ++i) v[k][i] = 0.f;
-            }
-            store_row12(out + (long)(tl.x + r) * D, lane, v[k]);
+            for (int i = 0; i < 12; ++i) v[k][i] = 0.f;
         }
+        const long dst = scatter ? (long)scatter[tl.x + r] : (long)(tl.x + r);
+        store_row12(out + dst * D, lane, v[k]);
     }
     if (partials == nullptr) return;
 #pragma unroll
@@ -140,8 +159,8 @@ __global__ __launch_bounds__(64 * FWAVES) void final_ln_kernel(const float* __re
     for (int col = threadIdx.x; col < D; col += 64 * FWAVES) {
         float sum = 0.f;
 #pragma unroll
-        for (int q = 0; q < FWAVES; ++q) sum += red[q][col];
-        partials[(long)b * D + col] = sum;
+        for (int qq = 0; qq < FWAVES; ++qq) sum += red[qq][col];
+        partials[(long)blockIdx.x * D + col] = sum;
     }
 }
 
@@ -161,8 +180,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const int* __restrict__ meta,
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
         const int col = threadIdx.x + 256 * c;
-        float acc = 0.f;
-        for (int b = t0; b < t1; ++b) acc += partials[(long)b * D + col];
+        float acc = 0.f;  // in order: tile, then quarter
+        for (int b = t0 * FPARTS; b < t1 * FPARTS; ++b) acc += partials[(long)b * D + col];
         m[c] = L > 0 ? acc / (float)L : 0.f;
         sq += m[c] * m[c];
     }
@@ -175,22 +194,22 @@ __global__ __launch_bounds__(256) void pool_kernel(const int* __restrict__ meta,
     for (int c = 0; c < 3; ++c) pooled[(long)s * D + threadIdx.x + 256 * c] = m[c] * inv;
 }
 
-// Column sums of one work tile of already-normalised rows (the mean pooling of a finished
-// forward), in the same fixed order as the final-norm kernel's partials.
+// Column sums of already-normalised rows (the mean pooling of a finished forward), per quarter
+// work tile and in the same fixed order as the final-norm kernel's partials.
 __global__ __launch_bounds__(64 * FWAVES) void colsum_kernel(const float* __restrict__ out,
                                                              const int* __restrict__ meta,
                                                              int total_max, int S,
                                                              float* __restrict__ partials) {
     __shared__ float red[FWAVES][D];
     const MetaView mv = meta_view(const_cast<int*>(meta), total_max, S);
-    const int b = blockIdx.x;
+    const int b = blockIdx.x / FPARTS, q = blockIdx.x % FPARTS;
     if (b >= mv.counts[MBERT_META_NTILES]) return;
     const int4 tl = mv.tiles[b];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float acc[12];
 #pragma unroll
     for (int i = 0; i < 12; ++i) acc[i] = 0.f;
-    for (int r = wave; r < tl.y; r += FWAVES) {
+    for (int r = q * FROWS + wave; r < min(tl.y, (q + 1) * FROWS); r += FWAVES) {
         float v[12];
         load_row12(out + (long)(tl.x + r) * D, lane, v);
 #pragma unroll
@@ -204,8 +223,8 @@ __global__ __launch_bounds__(64 * FWAVES) void colsum_kernel(const float* __rest
     for (int col = threadIdx.x; col < D; col += 64 * FWAVES) {
         float sum = 0.f;
 #pragma unroll
-        for (int q = 0; q < FWAVES; ++q) sum += red[q][col];
-        partials[(long)b * D + col] = sum;
+        for (int qq = 0; qq < FWAVES; ++qq) sum += red[qq][col];
+        partials[(long)blockIdx.x * D + col] = sum;
     }
 }
 
@@ -313,22 +332,27 @@ int launch_layernorm(mbert_dtype dt, const float* x, int total, const int32_t* m
 
 int launch_final_ln_pool(const float* resid, int total, const int32_t* meta, int n_seqs,
                          mbert_dtype dt, const void* w, float eps, float* out, float* pooled,
-                         float* partials, hipStream_t s) {
+                         float* partials, hipStream_t s, const int32_t* scatter,
+                         const int32_t* rowmap, int n_slots) {
     const size_t tmax = tiles_max_for(total, n_seqs);
-    if (tmax > 0) {
+    const int ln_blocks = (int)tmax * FPARTS;
+    // pad rows of the padded output: a wave per row, up to 512 workgroups striding over them
+    const int zero_blocks = (scatter && n_slots > 0) ? min((n_slots + 63) / 64, 512) : 0;
+    const unsigned grid = (unsigned)(ln_blocks + zero_blocks);
+    if (grid > 0) {
         float* part = pooled ? partials : nullptr;
         switch (dt) {
             case MBERT_F32:
-                MB_LAUNCH((final_ln_kernel<float>), (unsigned)tmax, 64 * FWAVES, 0, s, resid, meta, total, n_seqs,
-                                                                      (const float*)w, eps, out, part);
+                MB_LAUNCH((final_ln_kernel<float>), grid, 64 * FWAVES, 0, s, resid, meta, total, n_seqs,
+                          (const float*)w, eps, out, part, ln_blocks, scatter, rowmap, n_slots);
                 break;
             case MBERT_BF16:
-                MB_LAUNCH((final_ln_kernel<bf16>), (unsigned)tmax, 64 * FWAVES, 0, s, resid, meta, total, n_seqs,
-                                                                     (const bf16*)w, eps, out, part);
+                MB_LAUNCH((final_ln_kernel<bf16>), grid, 64 * FWAVES, 0, s, resid, meta, total, n_seqs,
+                          (const bf16*)w, eps, out, part, ln_blocks, scatter, rowmap, n_slots);
                 break;
             case MBERT_F16:
-                MB_LAUNCH((final_ln_kernel<f16>), (unsigned)tmax, 64 * FWAVES, 0, s, resid, meta, total, n_seqs,
-                                                                    (const f16*)w, eps, out, part);
+                MB_LAUNCH((final_ln_kernel<f16>), grid, 64 * FWAVES, 0, s, resid, meta, total, n_seqs,
+                          (const f16*)w, eps, out, part, ln_blocks, scatter, rowmap, n_slots);
                 break;
             default:
                 return MBERT_EUNSUPPORTED;
@@ -379,7 +403,8 @@ int launch_pool(const float* out, int total, const int32_t* meta, int n_seqs, in
     }
     const size_t tmax = tiles_max_for(total, n_seqs);
     if (tmax > 0) {
-        MB_LAUNCH((colsum_kernel), (unsigned)tmax, 64 * FWAVES, 0, s, out, meta, total, n_seqs, partials);
+        MB_LAUNCH((colsum_kernel), (unsigned)(tmax * FPARTS), 64 * FWAVES, 0, s, out, meta, total, n_seqs,
+                  partials);
         MB_CHECK_LAUNCH();
     }
     MB_LAUNCH((pool_kernel), n_seqs, 256, 0, s, meta, total, n_seqs, partials, pooled, normalize);
