@@ -288,8 +288,10 @@ __global__ __launch_bounds__(256) void unpad_compact_kernel(const int* __restric
 // pass over the B x Tpad slots in row-major chunks of 1024: a block-wide exclusive scan of the
 // real-token flags gives each real slot its packed row k (tokens are packed row by row, so k
 // counts the real slots before it), the first slot of row b records cu[b], and the position is
-// k - cu[b]. All mask and id loads are issued before the first scan.
+// k - cu[b]. All mask and id loads are issued before the first scan; cu_seqlens and the packed
+// rows stay in LDS and registers (no global round trip between the steps).
 constexpr int UNPAD_FUSED_CHUNKS = 16;  // slots per thread: up to 16 x 1024 slots
+constexpr int UNPAD_FUSED_SLOTS = UNPAD_FUSED_CHUNKS * 1024;
 __global__ __launch_bounds__(1024) void unpad_fused_kernel(const int* __restrict__ ids_pad,
                                                            const int* __restrict__ mask, int B,
                                                            int Tpad, int max_pos,
@@ -300,13 +302,14 @@ __global__ __launch_bounds__(1024) void unpad_fused_kernel(const int* __restrict
                                                            int* __restrict__ meta, int total_max) {
     __shared__ int lds[32];
     __shared__ int s_status, s_maxlen;
+    __shared__ int s_cu[UNPAD_FUSED_SLOTS + 1];  // the launcher keeps B <= UNPAD_FUSED_SLOTS
     const MetaView mv = meta_view(meta, total_max, B);
     const int n = B * Tpad, tid = threadIdx.x;
     if (tid == 0) {
         s_status = 0;
         s_maxlen = 0;
     }
-    int mv_[UNPAD_FUSED_CHUNKS] = {}, idv[UNPAD_FUSED_CHUNKS] = {};
+    int mv_[UNPAD_FUSED_CHUNKS] = {}, idv[UNPAD_FUSED_CHUNKS] = {}, kv[UNPAD_FUSED_CHUNKS] = {};
     if (n > 0) {
 #pragma unroll
         for (int c = 0; c < UNPAD_FUSED_CHUNKS; ++c) {
@@ -315,8 +318,11 @@ __global__ __launch_bounds__(1024) void unpad_fused_kernel(const int* __restrict
             idv[c] = ids_pad[slot];
         }
     }
-    if (Tpad == 0)
-        for (int b = tid; b <= B; b += blockDim.x) cu[b] = 0;
+    if (Tpad == 0)  // B rows without a slot: B empty sequences
+        for (int b = tid; b <= B; b += blockDim.x) {
+            s_cu[b] = 0;
+            cu[b] = 0;
+        }
     __syncthreads();
     int carry = 0, bad = 0;
 #pragma unroll
@@ -328,8 +334,12 @@ __global__ __launch_bounds__(1024) void unpad_fused_kernel(const int* __restrict
         bad |= in && mv_[c] != 0 && mv_[c] != 1;
         int tot;
         const int k = carry + block_excl_scan(real, lds, tot);
+        kv[c] = k;
         const int b = in ? slot / Tpad : 0;
-        if (in && slot == b * Tpad) cu[b] = k;
+        if (in && slot == b * Tpad) {
+            s_cu[b] = k;
+            cu[b] = k;
+        }
         if (in) {
             rowmap[slot] = real ? k : -1;
             if (real) {
@@ -339,22 +349,21 @@ __global__ __launch_bounds__(1024) void unpad_fused_kernel(const int* __restrict
         }
         carry += tot;
     }
-    if (tid == 0 && Tpad > 0) cu[B] = carry;
-    __syncthreads();  // every cu entry written
+    if (tid == 0 && Tpad > 0) {
+        s_cu[B] = carry;
+        cu[B] = carry;
+    }
+    __syncthreads();  // s_cu complete
     // positions: rank among the row's real tokens
 #pragma unroll
     for (int c = 0; c < UNPAD_FUSED_CHUNKS; ++c) {
         const int slot = c * 1024 + tid;
         if (c * 1024 >= n) break;
-        if (slot < n && mv_[c] != 0) {
-            const int b = slot / Tpad;
-            const int k = rowmap[slot];
-            mv.pos[k] = k - cu[b];
-        }
+        if (slot < n && mv_[c] != 0) mv.pos[kv[c]] = kv[c] - s_cu[slot / Tpad];
     }
     int status = bad ? MBERT_STATUS_BAD_MASK : 0, maxlen = 0;
     for (int b = tid; b < B; b += blockDim.x) {
-        const int L = cu[b + 1] - cu[b];
+        const int L = s_cu[b + 1] - s_cu[b];
         if (L > max_pos) status |= MBERT_STATUS_TOO_LONG;
         maxlen = max(maxlen, L);
     }
@@ -363,7 +372,7 @@ __global__ __launch_bounds__(1024) void unpad_fused_kernel(const int* __restrict
     __syncthreads();
     status = s_status;
     const bool ok = (status & MBERT_STATUS_TOO_LONG) == 0;
-    build_tiles(cu, B, ok, mv, lds);
+    build_tiles(s_cu, B, ok, mv, lds);
     if (tid == 0) {
         mv.counts[MBERT_META_TOTAL] = carry;
         mv.counts[MBERT_META_MAXLEN] = ok ? s_maxlen : 0;
@@ -446,7 +455,7 @@ int launch_unpad(const int32_t* ids_pad, const int32_t* mask, int B, int Tpad, i
                  int32_t* ids, int32_t* indices, int32_t* rowmap, int32_t* cu, int32_t* meta,
                  hipStream_t s) {
     const int total_max = B * Tpad;
-    if ((long)B * Tpad <= 1024L * UNPAD_FUSED_CHUNKS) {
+    if ((long)B * Tpad <= UNPAD_FUSED_SLOTS && B <= UNPAD_FUSED_SLOTS) {
         MB_LAUNCH((unpad_fused_kernel), 1, 1024, 0, s, ids_pad, mask, B, Tpad, max_pos, ids, indices, rowmap,
                   cu, meta, total_max);
         MB_CHECK_LAUNCH();

@@ -180,8 +180,15 @@ __global__ __launch_bounds__(256) void pool_kernel(const int* __restrict__ meta,
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
         const int col = threadIdx.x + 256 * c;
-        float acc = 0.f;  // in order: tile, then quarter
-        for (int b = t0 * FPARTS; b < t1 * FPARTS; ++b) acc += partials[(long)b * D + col];
+        float acc = 0.f;  // in order: tile, then quarter; eight loads in flight per batch
+        for (int b0 = t0 * FPARTS; b0 < t1 * FPARTS; b0 += 8) {
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                x[j] = b0 + j < t1 * FPARTS ? partials[(long)(b0 + j) * D + col] : 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc += x[j];
+        }
         m[c] = L > 0 ? acc / (float)L : 0.f;
         sq += m[c] * m[c];
     }
