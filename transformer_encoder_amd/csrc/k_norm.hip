@@ -57,8 +57,9 @@ __global__ __launch_bounds__(256) void embed_ln_kernel(const int* __restrict__ i
                                                        T* __restrict__ h) {
     const int lane = threadIdx.x & 63;
     const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= total) return;
+    int id = ids[row];  // loaded before the device row count is known: one round trip less
     if (row >= rows_of(counts, total)) return;
-    int id = ids[row];
     if (id < 0 || id >= vocab) {
         if (lane == 0 && counts) atomicOr(counts + MBERT_META_STATUS, MBERT_STATUS_BAD_ID);
         id = 0;
