@@ -17,13 +17,14 @@
 // columns = queries), so every lane owns one query column: the row max, row sum and the
 // rescaling of the output are per-lane, with one cross-lane exchange (lane ^ 32) for the max.
 // The probabilities then feed O^T = V^T P^T directly as the MFMA B operand (no shuffle);
-// V is stored transposed in LDS ([d][key]) so each lane's 8 keys are two 8-byte reads. The
-// MFMA k-slots of both operands follow the same key permutation (lane group g holds keys
-// 4g..4g+3 and 8+4g..8+4g+3 of each 16-key slice), which leaves the product unchanged.
+// V is staged in its natural [key][d] layout like K, and each lane's 8 keys at its d come
+// from two transposed LDS reads (ds_read_b64_tr_b16). The MFMA k-slots of both operands
+// follow the same key permutation (lane group g holds keys 4g..4g+3 and 8+4g..8+4g+3 of each
+// 16-key slice), which leaves the product unchanged.
 // Softmax is online in fp32 with exp2 and the scale 0.125 * log2(e) folded into one FMA; edge
 // tiles are masked branch-free; the running max is only raised (and the output rescaled) when a
 // row's max grows by more than 2^8.
-// The fp32 variant uses v_mfma_f32_32x32x2_f32 and keeps V in natural layout.
+// The fp32 variant uses v_mfma_f32_32x32x2_f32 and padded natural K and V rows.
 #include "common.hpp"
 
 // K/V tiles held in registers ahead of the LDS stage. One: a second stage gained 2-3 % on
@@ -49,7 +50,7 @@ template <typename T> struct AttnCfg {
     // XOR-swizzled by 16-byte chunk (kchunk): conflict-free both for the 16-byte row writes
     // and for the 16-byte reads of 16 rows at one chunk
     static constexpr int KP = F32 ? 68 : 64;
-    static constexpr int VP = 68;              // V pitch: fp32 [key][d], 16-bit [d][key]
+    static constexpr int VP = F32 ? 68 : 64;   // V pitch, [key][d]; 16-bit: unpadded, vchunk
     static constexpr int KSZ = 64 * KP;
     static constexpr int VSZ = 64 * VP;
 };
@@ -58,6 +59,19 @@ template <typename T> struct AttnCfg {
 // c ^ ((r >> 1) & 7); rows r and r + 1 differ by half of the 256-byte bank window, pairs of
 // rows by the slot.
 __device__ __forceinline__ int kchunk(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+// Transposed 8-byte LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane j gets
+// element j % 4 of the 4-element rows read by lanes j / 4, 4 + j / 4, 8 + j / 4, 12 + j / 4.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)p);
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// Byte offset of 16-byte chunk c of V row (key) r in the 16-bit layout: chunk c at slot
+// c ^ (4 * bit 1 of r). A transposed read takes four rows of 64 bytes (keys 4g.. of a 16-key
+// slice, d 32 db..) per half wave: the two rows of one parity land on disjoint slots.
+__device__ __forceinline__ int vchunk(int r, int c) { return r * 128 + ((c ^ (((r >> 1) & 1) << 2)) << 4); }
 
 template <typename T> struct Mma;
 template <> struct Mma<bf16> {
@@ -83,11 +97,11 @@ template <> struct Mma<f16> {
     }
 };
 
+// KS: key-tile sets per workgroup (1: 4 waves; 2: 8 waves, split keys, 16-bit types only)
 template <typename T, int KS>
-__global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(const T* __restrict__ qkv, T* __restrict__ out,
-                                                      const int* __restrict__ meta, int total_max,
-                                                      int S, int tiles_max, int is_global, int W,
-                                                      float scale_log2) {
+__global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(
+    const T* __restrict__ qkv, T* __restrict__ out, const int* __restrict__ meta, int total_max,
+    int S, int tiles_max, int is_global, int W, float scale_log2) {
     using C = AttnCfg<T>;
     constexpr bool F32 = C::F32;
     static_assert(KS == 1 || (KS == 2 && !F32), "key halves for the 16-bit types");
@@ -174,10 +188,9 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(const T
                 const int key = min(kb + (stid >> 3) + 32 * i, khi);
                 rk[u][i] = *(const u32x4*)(qkv + (size_t)key * QKV + D + head * HD + (stid & 7) * 8);
             }
-            const int kp = stid >> 3;  // key pair
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int key = min(kb + 2 * kp + i, khi);
+            for (int i = 0; i < KCH; ++i) {
+                const int key = min(kb + (stid >> 3) + 32 * i, khi);
                 rv[u][i] = *(const u32x4*)(qkv + (size_t)key * QKV + 2 * D + head * HD + (stid & 7) * 8);
             }
         }
@@ -194,18 +207,9 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(const T
 #pragma unroll
             for (int i = 0; i < KCH; ++i)
                 *(u32x4*)(reinterpret_cast<unsigned char*>(&Ks[st][sh][0]) + kchunk((stid >> 3) + 32 * i, stid & 7)) = rk[u][i];
-            // transpose: Vt[d][key]; one dword holds keys (2kp, 2kp+1) of one d. Rows 32-63
-            // store their keys at column key ^ 16 (dword kp ^ 8): without it the lanes writing
-            // rows d and d + 32 of one wave instruction hit the same banks
-            const int kp = stid >> 3, d0 = (stid & 7) * 8;
-            const int kps = kp ^ (d0 >= 32 ? 8 : 0);
-            unsigned* vt = reinterpret_cast<unsigned*>(&Vs[st][sh][0]);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const unsigned a = rv[u][0][m], b = rv[u][1][m];
-                vt[((d0 + 2 * m) * C::VP) / 2 + kps] = (a & 0xFFFFu) | (b << 16);
-                vt[((d0 + 2 * m + 1) * C::VP) / 2 + kps] = (a >> 16) | (b & 0xFFFF0000u);
-            }
+            for (int i = 0; i < KCH; ++i)
+                *(u32x4*)(reinterpret_cast<unsigned char*>(&Vs[st][sh][0]) + vchunk((stid >> 3) + 32 * i, stid & 7)) = rv[u][i];
         }
     };
 
@@ -324,16 +328,23 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(const T
                 for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                     for (int h = 0; h < 2; ++h) pb[kk][h] = Mma<T>::pack(&sv[16 * kk + 8 * h]);
+                // V^T fragments by transposed reads: in each 16-lane group, lane m reads the
+                // 4 values of V row 4g + m/4 (of the 16-key slice) at d 32 db + 16 (bit 4 of
+                // the lane) + 4 (m % 4); the read hands lane n the 4 keys 4g..4g+3 at d 32 db + n
+                const int m16 = lane & 15, q4 = lane >> 4;
+                const int rowoff = 4 * (q4 >> 1) + (m16 >> 2);
+                const int cb = 2 * (q4 & 1) + ((m16 >> 1) & 1), xsw = ((rowoff >> 1) & 1) << 2;
+                const unsigned char* vb =
+                    reinterpret_cast<const unsigned char*>(&Vs[st][kh][0]) + rowoff * 128 + (m16 & 1) * 8;
 #pragma unroll
                 for (int db = 0; db < 2; ++db)
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                         for (int h = 0; h < 2; ++h) {
-                            // rows 32-63 hold their keys at column ^ 16 (see sstore)
-                            const T* base = &Vs[st][kh][(32 * db + n) * C::VP + 32 * kk + 16 * (h ^ db) + 4 * g];
-                            const u32x2 lo = *(const u32x2*)base;
-                            const u32x2 hi = *(const u32x2*)(base + 8);
+                            const unsigned char* p = vb + (((4 * db + cb) ^ xsw) << 4) + (32 * kk + 16 * h) * 128;
+                            const u32x2 lo = lds_read_tr16(p);            // keys 4g .. 4g+3
+                            const u32x2 hi = lds_read_tr16(p + 8 * 128);  // keys 8+4g .. 8+4g+3
                             const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
                             Mma<T>::run(a, pb[kk][h], oacc[db]);
                         }
@@ -349,19 +360,21 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(const T
         // are free): waves 4-7 leave their running max, sum and output in LDS, waves 0-3 add
         // them in on the larger of the two maxima. A half that saw no key has max -inf and
         // weight 0.
-        float* xm = reinterpret_cast<float*>(&Vs[0][0][0]) + qg * 34 * 64 + lane;
-        static_assert(sizeof(Vs) >= 4 * 34 * 64 * sizeof(float), "merge area");
+        float* xs = reinterpret_cast<float*>(&Ks[0][0][0]) + qg * 2 * 64 + lane;  // max, sum
+        float* xm = reinterpret_cast<float*>(&Vs[0][0][0]) + qg * 32 * 64 + lane;  // outputs
+        static_assert(sizeof(Ks) >= 4 * 2 * 64 * sizeof(float) && sizeof(Vs) >= 4 * 32 * 64 * sizeof(float),
+                      "merge area");
         if (kh == 1) {
-            xm[0] = m_run;
-            xm[64] = l_run;
+            xs[0] = m_run;
+            xs[64] = l_run;
 #pragma unroll
             for (int db = 0; db < 2; ++db)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) xm[(2 + 16 * db + e) * 64] = oacc[db][e];
+                for (int e = 0; e < 16; ++e) xm[(16 * db + e) * 64] = oacc[db][e];
         }
         __syncthreads();
         if (kh == 1) return;
-        const float m1 = xm[0], l1 = xm[64];
+        const float m1 = xs[0], l1 = xs[64];
         const float mm = fmaxf(m_run, m1);
         const float f0 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
         const float f1 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
@@ -369,7 +382,7 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(const T
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) oacc[db][e] = oacc[db][e] * f0 + xm[(2 + 16 * db + e) * 64] * f1;
+            for (int e = 0; e < 16; ++e) oacc[db][e] = oacc[db][e] * f0 + xm[(16 * db + e) * 64] * f1;
     }
 
     // ---- normalise and write: lane holds d = 32 db + 8 j + 4 g + i of its query
