@@ -301,6 +301,7 @@ __global__ __launch_bounds__(1024) void unpad_fused_kernel(const int* __restrict
                                                            int* __restrict__ cu,
                                                            int* __restrict__ meta, int total_max) {
     __shared__ int lds[32];
+    __shared__ int wcnt[16];  // real slots per wave of the current chunk
     __shared__ int s_status, s_maxlen;
     __shared__ int s_cu[UNPAD_FUSED_SLOTS + 1];  // the launcher keeps B <= UNPAD_FUSED_SLOTS
     const MetaView mv = meta_view(meta, total_max, B);
@@ -332,8 +333,22 @@ __global__ __launch_bounds__(1024) void unpad_fused_kernel(const int* __restrict
         const bool in = slot < n;
         const int real = in && mv_[c] != 0;
         bad |= in && mv_[c] != 0 && mv_[c] != 1;
-        int tot;
-        const int k = carry + block_excl_scan(real, lds, tot);
+        // exclusive prefix of the 0/1 flags: ballot and population count within the wave, then
+        // the counts of the waves before it
+        const int lane = tid & 63, wv = tid >> 6;
+        const unsigned long long bal = __ballot(real);
+        const int below = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) wcnt[wv] = __popcll(bal);
+        __syncthreads();
+        int woff = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const int cw = wcnt[w];
+            woff += w < wv ? cw : 0;
+            tot += cw;
+        }
+        __syncthreads();  // wcnt is rewritten by the next chunk
+        const int k = carry + woff + below;
         kv[c] = k;
         const int b = in ? slot / Tpad : 0;
         if (in && slot == b * Tpad) {
