@@ -3,10 +3,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
 
 A step is one whole forward of the 22-layer encoder over one batch of synthetic input already
-resident in HBM: unpad -> embedding + LN -> 22 layers -> final LN + pooling -> re-pad for the
-padded workload 2 (batch 8, lengths uniform in [128, 512], padded to 512, bf16, random-init
-weights). The timed region replays the forward captured as one HIP graph (the eager rate is
-reported beside it). Prints one JSON line.
+resident in HBM: unpad -> embedding + LN -> 22 layers -> final LN into the padded output +
+pooling, for the padded workload 2 (batch 8, lengths uniform in [128, 512], padded to 512,
+bf16, random-init weights). The timed region replays the forward captured as one HIP graph,
+the batch split into three groups of whole sequences on three streams (`--groups`); the eager
+and one-stream rates are reported beside it. Prints one JSON line.
 
 Per-kernel roofline: every launch of the dominant kernel (the kind with the largest share of
 one eager forward) is bracketed with HIP events on the stream it runs on, over the eager timed

@@ -305,10 +305,10 @@ int mbert_encode(const mbert_weights* w, const int32_t* ids, const int32_t* cu_s
                  float* pooled, void* stream);
 
 /* mbert_encode_padded: padded batch ids_pad/mask [B,Tpad] on the device: unpad, encode,
- * re-pad. out_pad [B,Tpad,768] f32 with zeros at pads; pooled [B,768] (may be NULL). The
- * packed result stays in the workspace (layout.out) and the packed cu_seqlens/indices in
- * layout.cu/layout.indices. No host synchronisation: the token count stays on the device.
- * Workspace from mbert_workspace_bytes(cfg, dtype, B*Tpad, B). */
+ * re-pad. out_pad [B,Tpad,768] f32 with zeros at pads (the final LayerNorm writes each token's
+ * row to its padded slot); pooled [B,768] (may be NULL). The packed cu_seqlens/indices stay
+ * in the workspace (layout.cu/layout.indices). No host synchronisation: the token count stays
+ * on the device. Workspace from mbert_workspace_bytes(cfg, dtype, B*Tpad, B). */
 int mbert_encode_padded(const mbert_weights* w, const int32_t* ids_pad, const int32_t* mask,
                         int B, int Tpad, void* ws, size_t ws_bytes, float* out_pad,
                         float* pooled, void* stream);
