@@ -340,6 +340,33 @@ def test_attention_long_global(dtype):
         assert rel_err(host(o), ref) < TOL_STEP[dtype]
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_attention_random_length_mixes(seed, dtype):
+    """Seeded random batches (2-8 sequences of 0-300 tokens, or 2-40 of 0-700: empty
+    sequences, single tokens, ragged tails and multi-tile sequences mixed) on both layer kinds
+    and several windows; the grid sizes fall on both sides of the split-key bound (256 work
+    groups)."""
+    g = np.random.default_rng(1000 + seed)
+    small = seed < 2  # small batches: grids under the bound
+    S = int(g.integers(2, 9 if small else 41))
+    lengths = [int(x) for x in g.integers(0, 301 if small else 701, size=S)]
+    lengths[int(g.integers(0, S))] = int(g.integers(0, 2))
+    cu = cu_from_lengths(lengths)
+    T = int(cu[-1])
+    if T == 0:
+        pytest.skip("empty batch")
+    qkv = random_matrix((T, 2304), 95 + seed, dtype=dtype, std=1.5)
+    W = int(g.choice([64, 17, 1]))
+    for glob in (True, False):
+        o = torch().full((T, 768), float("nan"), dtype=_tdt(dtype), device="cuda")
+        B().mbert_attention(dt(dtype), dev(qkv, dtype), T, meta_for(cu, T), S, glob, W, o)
+        ref = O.attention_varlen(qkv, O.segments_of(cu), glob, O.Config(half_window=W))
+        got = host(o)
+        assert np.all(np.isfinite(got)), (lengths, glob, W)
+        assert rel_err(got, ref) < TOL_STEP[dtype], (lengths, glob, W)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("glob", [True, False], ids=["global", "local"])
 def test_attention_split_and_whole_agree(dtype, glob):
