@@ -25,6 +25,25 @@ __device__ __forceinline__ void store_row12(T* row, int lane, const float v[12])
                        make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]));
 }
 
+// The same row written through to memory as it retires (buffer stores with sc1): each store
+// instruction covers whole 128-byte lines, so no dirty line is left in L2 for the write-back
+// at the end of the kernel, which the next kernel would wait for.
+template <typename T>
+__device__ __forceinline__ void store_row12_wt(T* row, int lane, const float v[12]) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        const unsigned off = (unsigned)(sizeof(T) * 4 * (lane + 64 * c));
+        if constexpr (sizeof(T) == 4) {
+            const f32x4 o = {v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
+            buf_store16(__builtin_bit_cast(u32x4, o), row, D * 4, off);
+        } else {
+            typedef T t4 __attribute__((ext_vector_type(4)));
+            const t4 o = {(T)v[4 * c], (T)v[4 * c + 1], (T)v[4 * c + 2], (T)v[4 * c + 3]};
+            buf_store8b(__builtin_bit_cast(unsigned long long, o), row, D * (unsigned)sizeof(T), off);
+        }
+    }
+}
+
 // Weight-only LayerNorm of one row held by a wave: mean, biased variance from a second pass,
 // eps inside the square root, times the weight (kgptalkie, "ModernBERT-base Architecture
 // Teardown", §"What Does LayerNorm Do?"; candding, "ModernBERT", §"The pre-norm layer and the
@@ -67,8 +86,10 @@ __global__ __launch_bounds__(256) void embed_ln_kernel(const int* __restrict__ i
     float v[12];
     load_row12(emb + (long)id * D, lane, v);
     layernorm12(v, w, lane, eps);
-    store_row12(resid + row * D, lane, v);
-    if (h != nullptr && (void*)h != (void*)resid) store_row12(h + row * D, lane, v);
+    // the row index as a wave-uniform value for the stores' buffer descriptors
+    const long urow = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    store_row12_wt(resid + urow * D, lane, v);
+    if (h != nullptr && (void*)h != (void*)resid) store_row12_wt(h + urow * D, lane, v);
 }
 
 template <typename T>
@@ -93,7 +114,9 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
 // full width) are written as zeros and left out of the sums.
 // With `scatter`, packed row k is written to row scatter[k] of `out` (the padded output), and
 // the workgroups after the LayerNorm ones write zeros to every row whose rowmap entry is
-// negative (the pads): the re-pad is part of this launch.
+// negative (the pads): the re-pad is part of this launch. There a wave takes 64 consecutive
+// slots, reads their rowmap entries with one load and zeroes the pad rows among them, so no
+// wave waits on more than one load.
 constexpr int FROWS = TILE / FPARTS;    // rows per workgroup
 constexpr int FWAVES = 4;
 constexpr int FRW = FROWS / FWAVES;     // rows per wave
@@ -112,16 +135,24 @@ __global__ __launch_bounds__(64 * FWAVES) void final_ln_kernel(const float* __re
     __shared__ float red[FWAVES][D];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if ((int)blockIdx.x >= ln_blocks) {  // pad rows of the padded output
+        const int r0 = (((int)blockIdx.x - ln_blocks) * FWAVES + wave) * 64;
+        if (r0 >= n_slots) return;
+        unsigned long long pads = __ballot(r0 + lane < n_slots && rowmap[r0 + lane] < 0);
         const float z[12] = {};
-        const int stride = (gridDim.x - ln_blocks) * FWAVES;
-        for (int r = ((int)blockIdx.x - ln_blocks) * FWAVES + wave; r < n_slots; r += stride)
-            if (rowmap[r] < 0) store_row12(out + (long)r * D, lane, z);
+        while (pads) {  // wave-uniform
+            const int j = __builtin_ctzll(pads);
+            pads &= pads - 1;
+            store_row12(out + (long)(r0 + j) * D, lane, z);
+        }
         return;
     }
     const MetaView mv = meta_view(const_cast<int*>(meta), total_max, S);
     const int b = blockIdx.x / FPARTS, q = blockIdx.x % FPARTS;
-    if (b >= mv.counts[MBERT_META_NTILES]) return;
+    // the tile entry (b < tiles_max: in bounds) is read beside the tile count, not after it;
+    // a real tile never has fewer than one row, so the second test only keeps both loads
+    // ahead of the branch
     const int4 tl = mv.tiles[b];
+    if ((b >= mv.counts[MBERT_META_NTILES]) | (tl.y < 1)) return;
     const int r0 = q * FROWS;
     if (r0 >= tl.y) {  // an empty quarter still leaves its (zero) partial sums
         if (partials)
@@ -130,9 +161,13 @@ __global__ __launch_bounds__(64 * FWAVES) void final_ln_kernel(const float* __re
     }
     const int real = min(tl.y, tl.w - tl.x);
     float v[FRW][12];
+    long dst[FRW];  // output rows, loaded with the input rows
 #pragma unroll
-    for (int k = 0; k < FRW; ++k)
-        load_row12(resid + (long)(tl.x + min(r0 + wave + FWAVES * k, tl.y - 1)) * D, lane, v[k]);
+    for (int k = 0; k < FRW; ++k) {
+        const int r = tl.x + min(r0 + wave + FWAVES * k, tl.y - 1);
+        load_row12(resid + (long)r * D, lane, v[k]);
+        dst[k] = scatter ? (long)scatter[r] : (long)r;
+    }
     float acc[12];
 #pragma unroll
     for (int i = 0; i < 12; ++i) acc[i] = 0.f;
@@ -148,8 +183,7 @@ __global__ __launch_bounds__(64 * FWAVES) void final_ln_kernel(const float* __re
 #pragma unroll
             for (int i = 0; i < 12; ++i) v[k][i] = 0.f;
         }
-        const long dst = scatter ? (long)scatter[tl.x + r] : (long)(tl.x + r);
-        store_row12(out + dst * D, lane, v[k]);
+        store_row12(out + dst[k] * D, lane, v[k]);
     }
     if (partials == nullptr) return;
 #pragma unroll
@@ -176,21 +210,27 @@ __global__ __launch_bounds__(256) void pool_kernel(const int* __restrict__ meta,
     const int s = blockIdx.x;
     const int t0 = mv.seq_tile0[s], t1 = mv.seq_tile0[s + 1];
     const int L = t1 > t0 ? mv.tiles[t0].w - mv.tiles[t0].z : 0;
+    // each column summed in order (tile, then quarter); a batch holds 16 partial rows of all
+    // three of the thread's columns, 48 loads in flight
+    constexpr int PB = 16;
+    float acc[3] = {0.f, 0.f, 0.f};
+    for (int b0 = t0 * FPARTS; b0 < t1 * FPARTS; b0 += PB) {
+        float x[PB][3];
+#pragma unroll
+        for (int j = 0; j < PB; ++j)
+#pragma unroll
+            for (int c = 0; c < 3; ++c)
+                x[j][c] = b0 + j < t1 * FPARTS ? partials[(long)(b0 + j) * D + threadIdx.x + 256 * c] : 0.f;
+#pragma unroll
+        for (int j = 0; j < PB; ++j)
+#pragma unroll
+            for (int c = 0; c < 3; ++c) acc[c] += x[j][c];
+    }
     float m[3];
     float sq = 0.f;
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
-        const int col = threadIdx.x + 256 * c;
-        float acc = 0.f;  // in order: tile, then quarter; eight loads in flight per batch
-        for (int b0 = t0 * FPARTS; b0 < t1 * FPARTS; b0 += 8) {
-            float x[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                x[j] = b0 + j < t1 * FPARTS ? partials[(long)(b0 + j) * D + col] : 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc += x[j];
-        }
-        m[c] = L > 0 ? acc / (float)L : 0.f;
+        m[c] = L > 0 ? acc[c] / (float)L : 0.f;
         sq += m[c] * m[c];
     }
     sq = wave_sum(sq);
@@ -344,8 +384,8 @@ int launch_final_ln_pool(const float* resid, int total, const int32_t* meta, int
                          const int32_t* rowmap, int n_slots) {
     const size_t tmax = tiles_max_for(total, n_seqs);
     const int ln_blocks = (int)tmax * FPARTS;
-    // pad rows of the padded output: a wave per row, up to 512 workgroups striding over them
-    const int zero_blocks = (scatter && n_slots > 0) ? min((n_slots + 63) / 64, 512) : 0;
+    // pad rows of the padded output: a wave per 64 slots
+    const int zero_blocks = (scatter && n_slots > 0) ? (n_slots + 64 * FWAVES - 1) / (64 * FWAVES) : 0;
     const unsigned grid = (unsigned)(ln_blocks + zero_blocks);
     if (grid > 0) {
         float* part = pooled ? partials : nullptr;
