@@ -154,6 +154,41 @@ def test_edge_batches_two_layers(lengths, dtype, fold):
             assert np.all(host(pooled)[i] == 0)
 
 
+@pytest.mark.parametrize("lengths,tpad", [([37, 0, 5], 37), ([200, 1], 200), ([64, 3, 0, 64, 10], 64)],
+                         ids=["3x37", "2x200", "5x64"])
+def test_padded_ragged_slots_zero_pads(lengths, tpad):
+    """Padded forward on slot counts that are not multiples of 64 (111, 400, 320), into
+    outputs filled with NaN first: every pad row comes back exactly zero, every real row and
+    pooled vector matches the oracle (an empty row pools to zero)."""
+    from transformer_encoder_amd import binding as B
+    from transformer_encoder_amd.model import DeviceModel
+    w = make_weights(Dims(n_layers=2), "bf16", 900 + len(lengths))
+    b = random_batch(lengths, 91)
+    Bn = len(lengths)
+    ids_pad = np.full((Bn, tpad), 50283, np.int32)
+    mask = np.zeros((Bn, tpad), np.int32)
+    for i, L in enumerate(lengths):
+        ids_pad[i, :L] = b["ids"][b["cu_seqlens"][i]:b["cu_seqlens"][i + 1]]
+        mask[i, :L] = 1
+    m = DeviceModel(w, "bf16")
+    t = torch()
+    out = t.full((Bn, tpad, 768), float("nan"), device="cuda")
+    pool = t.full((Bn, 768), float("nan"), device="cuda")
+    ws = m.workspace(Bn * tpad, Bn)
+    B.mbert_encode_padded(m.w, dev_i32(ids_pad), dev_i32(mask), Bn, tpad, ws, ws.numel(), out, pool,
+                          None)
+    got, gpool = host(out), host(pool)
+    ref, rpool = O.encode(b["ids"], b["cu_seqlens"], w, O.Config(n_layers=2))
+    real = mask.astype(bool)
+    assert np.all(got[~real] == 0.0), "pad rows not zeroed"
+    check_16bit(got[real], ref, f"padded {Bn}x{tpad} tokens")
+    nz = [i for i, L in enumerate(lengths) if L > 0]
+    check_16bit(gpool[nz], rpool[nz], f"padded {Bn}x{tpad} pooled")
+    for i, L in enumerate(lengths):
+        if L == 0:
+            assert np.all(gpool[i] == 0.0)
+
+
 def test_deterministic_and_graph_replay():
     from transformer_encoder_amd import binding as B
     wl = WORKLOADS[2]
