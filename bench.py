@@ -76,8 +76,10 @@ def kernel_work(kind, T, lengths, dtype_bytes, n_layers=22, n_global=8):
 
 
 def source_hash() -> str:
+    """Hash of the kernel sources and the build script (whose flags shape the kernels)."""
     h = hashlib.sha256()
-    for p in sorted((ROOT / "transformer_encoder_amd" / "csrc").glob("*")):
+    pkg = ROOT / "transformer_encoder_amd"
+    for p in [*sorted((pkg / "csrc").glob("*")), pkg / "build.py"]:
         h.update(p.name.encode())
         h.update(p.read_bytes())
     return h.hexdigest()[:16]
