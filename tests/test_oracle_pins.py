@@ -124,6 +124,53 @@ def test_zero_pad_masked_is_invisible_unmasked_is_not():
     assert np.max(np.abs(unmasked[:3] - alone)) > 1e-3
 
 
+def _whole_band_attention(q, k, v, is_global, W, key_valid):
+    """The plain definition over the whole sequence at once: one [L, L] allowed matrix, no
+    query blocks and no clipped key window."""
+    L, H, _ = q.shape
+    pos = np.arange(L)
+    allowed = O.band_allowed(pos, pos, is_global, W)
+    if key_valid is not None:
+        allowed = allowed & np.asarray(key_valid, bool)[None, :]
+    out = np.zeros_like(q)
+    for h in range(H):
+        out[:, h] = O.attention_probs(q[:, h], k[:, h], allowed) @ v[:, h]
+    return out
+
+
+@pytest.mark.parametrize("L", [1025, 2300])
+@pytest.mark.parametrize("is_global,W", [(True, 64), (False, 64), (False, 3)])
+@pytest.mark.parametrize("masked", [False, True], ids=["all_keys", "key_mask"])
+def test_attention_sequence_blocking_equals_whole_band(L, is_global, W, masked):
+    """The oracle's attention walks queries in chunks and, on local layers, scores only the
+    keys [a - W, b + W) that a chunk [a, b) can reach. Both are bookkeeping: for every chunk
+    size the result must be the plain whole-sequence definition (kgptalkie, "How Does
+    Self-Attention Work?"; candding, "ModernBERT", "The alternating attention": a key j is
+    read by query i iff |i - j| <= W). Chunks of 1 and 7 put boundaries everywhere, 1024 is
+    the default (a ragged last chunk at L = 1025 and 2300), L is one chunk. An off-by-one in
+    the clipped window drops or adds the edge key of a chunk's first or last query."""
+    rng = np.random.default_rng([L, W, int(is_global), int(masked)])
+    H, hd = 2, 8
+    q, k, v = (2.0 * rng.standard_normal((L, H, hd)) for _ in range(3))
+    key_valid = None
+    if masked:
+        key_valid = rng.random(L) > 0.3
+        key_valid[:: 97] = True  # every local band keeps some real key
+    ref = _whole_band_attention(q, k, v, is_global, W, key_valid)
+    for chunk in (1, 7, 1024, L):
+        got = O.attention_sequence(q, k, v, is_global, W, key_valid=key_valid, chunk=chunk)
+        assert np.max(np.abs(got - ref)) <= 1e-12, chunk
+    # the comparison is sharp: dropping the last key of each chunk's window is caught
+    if not is_global:
+        pos = np.arange(L)
+        a, b = 0, 7
+        allowed = O.band_allowed(pos[a:b], pos[max(0, a - W):b + W - 1], False, W)
+        p = O.attention_probs(q[a:b, 0], k[max(0, a - W):b + W - 1, 0], allowed)
+        wrong = p @ v[max(0, a - W):b + W - 1, 0]
+        if not masked:
+            assert np.max(np.abs(wrong[-1] - ref[b - 1, 0])) > 1e-6
+
+
 # ------------------------------------------------------------------------------ window / schedule
 def test_global_layer_schedule():
     g = gold("window_counts.json")
