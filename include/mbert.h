@@ -104,16 +104,21 @@ typedef struct {
  * with mean and rstd of each row of x (biased variance, eps inside the square root). The
  * residual GEMMs then also write each row's statistics per 64-column chunk and the residual
  * rounded to dtype, and no separate LayerNorm kernel runs between them. Only the rounding
- * point moves: dtype(x) enters the GEMM instead of dtype(LN(x)); the two agree as long as a
- * row's mean is not large against its spread. MBERT_F16 is not folded: the raw residual of a
- * trained model can exceed the fp16 range, while its normalised values cannot.
+ * point moves: dtype(x) enters the GEMM instead of dtype(LN(x)). The rounding error of x is
+ * relative to |x|, that of LN(x) to the row's spread, so the two agree while a row's mean is
+ * small against its spread: the normalised error grows like |mean| / std times one unit of
+ * the dtype (2^-9 bf16, 2^-12 fp16), i.e. cancellation in x - mean, not range. Magnitude
+ * alone is harmless: the fp32 residual and its chunk statistics stay exact, and a trained
+ * model's residual stream peaks near 81 % of the fp16 maximum (candding §"Dtype headroom"),
+ * which fp16 holds; a residual beyond 65,504 would overflow the fp16 copy, and such a model
+ * must run with folded = NULL (separate LayerNorms from the fp32 residual).
  * mbert_fold_norms fills `folded` (mbert_folded_bytes(cfg, dtype) bytes, device) from w's
  * current weights; setting w->folded to it makes mbert_encode, mbert_encode_padded and
  * mbert_encode_padded_keymask (and their graph captures) use the folded path; mbert_layer
  * always runs the separate LayerNorm. Re-run after changing a Wqkv, Wi or norm weight.
  * Layout per layer l: Wqkv o attn_norm [2304,768] dtype, its c [2304] f32, Wi o mlp_norm
  * [2304,768] dtype, its c [2304] f32, each 256-byte aligned (layer 0's first two unused).
- * Returns MBERT_EUNSUPPORTED for MBERT_F16, MBERT_ENOSPC if bytes is too small. */
+ * Returns MBERT_ENOSPC if bytes is too small. */
 size_t mbert_folded_bytes(const mbert_config* cfg, mbert_dtype dtype);
 int mbert_fold_norms(const mbert_weights* w, void* folded, size_t bytes, void* stream);
 
@@ -219,6 +224,30 @@ int mbert_linear_residual(mbert_dtype dtype, const void* a, int K, int total,
  * feed-forward halves"; kgptalkie §"What Does the GeGLU MLP Do?"). */
 int mbert_mlp_in_geglu(mbert_dtype dtype, const void* h, int total, const int32_t* meta,
                        const void* Wi, void* m, void* stream);
+
+/* The folded path one step at a time (the same kernels the folded forward runs).
+ * mbert_linear_residual_stats: resid += a . W^T as mbert_linear_residual, and also
+ * stats [T,12,2] f32 = {mean, sum of squared deviations from it} of each 64-column chunk of
+ * each new residual row, and xs [T,768] dtype = the new residual rounded once to dtype
+ * (16-bit types; ignored for MBERT_F32, whose folded GEMM reads resid itself).
+ * mbert_fold_weight: Wf [rows,768] dtype = W o w (each column k scaled by the norm weight
+ * w[k], rounded once), c [rows] f32 = the sum of each rounded row of Wf.
+ * mbert_folded_gemm: LN(x; w) . W^T computed as rstd * (xs . Wf^T - mean * c), mean and rstd
+ * merged from the chunk statistics (Chan et al.'s pairwise formula; biased variance, eps
+ * inside the square root). kind MBERT_FOLD_QKV_ROPE: Wf from Wqkv, out = qkv [T,2304] with
+ * RoPE as mbert_qkv_rope (apply_rope = 1; meta, rope, table required); kind
+ * MBERT_FOLD_GEGLU: Wf from Wi, out = m [T,1152] as mbert_mlp_in_geglu. For MBERT_F32 pass
+ * the fp32 residual as xs. */
+#define MBERT_FOLD_QKV_ROPE 0
+#define MBERT_FOLD_GEGLU 1
+int mbert_linear_residual_stats(mbert_dtype dtype, const void* a, int K, int total,
+                                const int32_t* meta, const void* W, float* resid, void* xs,
+                                float* stats, void* stream);
+int mbert_fold_weight(mbert_dtype dtype, const void* W, const void* w, int rows, void* Wf,
+                      float* c, void* stream);
+int mbert_folded_gemm(mbert_dtype dtype, int kind, const void* xs, const float* stats, int total,
+                      const int32_t* meta, const void* Wf, const float* c, float eps,
+                      const float* rope, int max_positions, int table, void* out, void* stream);
 
 /* Final LayerNorm and pooling: out [T,768] f32 = LN(resid; w); pooled [S,768] f32 = the mean
  * of each sequence's rows of out divided by max(L2 norm, 1e-12); an empty sequence pools to

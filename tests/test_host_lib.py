@@ -180,23 +180,37 @@ def test_step_validation_paths(lib):
     assert clf(1, fake, 4, fake, fake, 1e-5, fake, fake, 4, fake, need - 1, fake, None) == B.MBERT_ENOSPC
     assert clf(1, fake, 0, None, None, 1e-5, None, None, 4, None, 0, None, None) == B.MBERT_OK
     assert lib.mbert_timer_create(0, ctypes.byref(ctypes.c_void_p())) == B.MBERT_EINVAL
+    # the folded path's step entry points
+    lrs = lib.mbert_linear_residual_stats
+    assert lrs(1, fake, 1000, 10, None, fake, fake, fake, fake, None) == B.MBERT_EUNSUPPORTED
+    assert lrs(1, fake, 768, 10, None, fake, fake, None, fake, None) == B.MBERT_EINVAL  # no xs
+    assert lrs(1, fake, 768, 10, None, fake, fake, fake, None, None) == B.MBERT_EINVAL  # no stats
+    assert lib.mbert_fold_weight(1, fake, None, 4, fake, fake, None) == B.MBERT_EINVAL
+    assert lib.mbert_fold_weight(1, None, None, 0, None, None, None) == B.MBERT_OK
+    fg = lib.mbert_folded_gemm
+    assert fg(1, 2, fake, fake, 10, fake, fake, fake, 1e-5, fake, 8192, 0, fake, None) == B.MBERT_EINVAL
+    assert fg(1, 0, fake, fake, 10, None, fake, fake, 1e-5, fake, 8192, 0, fake, None) == B.MBERT_EINVAL
+    assert fg(1, 1, fake, None, 10, fake, fake, fake, 1e-5, None, 0, 0, fake, None) == B.MBERT_EINVAL
+    assert fg(9, 1, fake, fake, 10, fake, fake, fake, 1e-5, None, 0, 0, fake, None) == B.MBERT_EUNSUPPORTED
 
 
 def test_fold_norms_sizes_and_validation(lib):
     """Folded-norm weights: one [2304,768] weight and [2304] column sums per norm, 256-byte
-    aligned, per layer; fp16 is not folded; every failure below returns before any launch."""
+    aligned, per layer, for every dtype; every failure below returns before any launch."""
     w = _fake_weights(n_layers=3)
     al = lambda n: (n + 255) // 256 * 256
     per = lambda ds: 2 * (al(2304 * 768 * ds) + al(2304 * 4))
     assert B.mbert_folded_bytes(w.cfg, B.MBERT_BF16) == 3 * per(2)
     assert B.mbert_folded_bytes(w.cfg, B.MBERT_F32) == 3 * per(4)
-    assert B.mbert_folded_bytes(w.cfg, B.MBERT_F16) == 0
+    assert B.mbert_folded_bytes(w.cfg, B.MBERT_F16) == 3 * per(2)
     need = B.mbert_folded_bytes(w.cfg, B.MBERT_BF16)
     fake = 0x4000
     assert lib.mbert_fold_norms(ctypes.byref(w), None, need, None) == B.MBERT_EINVAL
     assert lib.mbert_fold_norms(ctypes.byref(w), fake, need - 1, None) == B.MBERT_ENOSPC
-    assert lib.mbert_fold_norms(ctypes.byref(_fake_weights(dtype=B.MBERT_F16)), fake, need,
-                                None) == B.MBERT_EUNSUPPORTED
+    w16 = _fake_weights(dtype=B.MBERT_F16)
+    need16 = B.mbert_folded_bytes(w16.cfg, B.MBERT_F16)
+    assert need16 == 2 * per(2)
+    assert lib.mbert_fold_norms(ctypes.byref(w16), fake, need16 - 1, None) == B.MBERT_ENOSPC
     assert lib.mbert_fold_norms(None, fake, need, None) == B.MBERT_EINVAL
     # the forward's workspace holds the rounded residual and its chunk statistics
     L = B.mbert_workspace_layout(w.cfg, B.MBERT_BF16, 1000, 4)

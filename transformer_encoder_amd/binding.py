@@ -79,6 +79,9 @@ _SIGNATURES = {
     "mbert_attention": ([I, P, I, P, I, I, I, P, P], I),
     "mbert_linear_residual": ([I, P, I, I, P, P, P, P], I),
     "mbert_mlp_in_geglu": ([I, P, I, P, P, P, P], I),
+    "mbert_linear_residual_stats": ([I, P, I, I, P, P, P, P, P, P], I),
+    "mbert_fold_weight": ([I, P, P, I, P, P, P], I),
+    "mbert_folded_gemm": ([I, I, P, P, I, P, P, P, c_float, P, I, I, P, P], I),
     "mbert_pool_partial_floats": ([I, I], SZ),
     "mbert_final_ln_pool": ([P, I, P, I, I, P, c_float, P, P, P, P], I),
     "mbert_repad": ([P, P, I, I, P, P], I),
@@ -262,6 +265,24 @@ def mbert_linear_residual(dtype, a, K, total, meta, W, resid, stream=None):
 def mbert_mlp_in_geglu(dtype, h, total, meta, Wi, m, stream=None):
     _call("mbert_mlp_in_geglu", dtype, ptr(h), total, ptr(meta), ptr(Wi), ptr(m),
           stream_handle(stream))
+
+
+FOLD_QKV_ROPE, FOLD_GEGLU = 0, 1
+
+
+def mbert_linear_residual_stats(dtype, a, K, total, meta, W, resid, xs, stats, stream=None):
+    _call("mbert_linear_residual_stats", dtype, ptr(a), K, total, ptr(meta), ptr(W), ptr(resid),
+          ptr(xs), ptr(stats), stream_handle(stream))
+
+
+def mbert_fold_weight(dtype, W, w, rows, Wf, c, stream=None):
+    _call("mbert_fold_weight", dtype, ptr(W), ptr(w), rows, ptr(Wf), ptr(c), stream_handle(stream))
+
+
+def mbert_folded_gemm(dtype, kind, xs, stats, total, meta, Wf, c, eps, rope, max_positions, table,
+                      out, stream=None):
+    _call("mbert_folded_gemm", dtype, kind, ptr(xs), ptr(stats), total, ptr(meta), ptr(Wf), ptr(c),
+          eps, ptr(rope), max_positions, table, ptr(out), stream_handle(stream))
 
 
 def mbert_pool_partial_floats(total_max, n_seqs) -> int:

@@ -160,7 +160,7 @@ FoldLayout fold_layout(mbert_dtype dt) {
     f.stride = 2 * (wbytes + cbytes);
     return f;
 }
-bool use_fold(const mbert_weights* w) { return w->folded != nullptr && w->dtype != MBERT_F16; }
+bool use_fold(const mbert_weights* w) { return w->folded != nullptr; }
 
 // One layer with the pre-norm LayerNorms folded into the QKV and Wi GEMMs: the residual
 // GEMMs leave the residual rounded to dtype (xs; for fp32 the residual itself) and its chunk
@@ -544,6 +544,43 @@ int mbert_mlp_in_geglu(mbert_dtype dt, const void* h, int total, const int32_t* 
     return mbh::launch_geglu(dt, h, total, meta, Wi, m, as_stream(stream));
 }
 
+int mbert_linear_residual_stats(mbert_dtype dt, const void* a, int K, int total,
+                                const int32_t* meta, const void* W, float* resid, void* xs,
+                                float* stats, void* stream) {
+    MB_TRY(check_dtype(dt));
+    MB_TRY(check_sizes(total, 0));
+    if (K != D && K != FF) return MBERT_EUNSUPPORTED;
+    if (total > 0 && (!a || !W || !resid || !stats || (dt != MBERT_F32 && !xs))) return MBERT_EINVAL;
+    return mbh::launch_linear_residual(dt, a, K, total, meta, W, resid, as_stream(stream),
+                                       dt == MBERT_F32 ? nullptr : xs,
+                                       reinterpret_cast<float2*>(stats));
+}
+
+int mbert_fold_weight(mbert_dtype dt, const void* W, const void* w, int rows, void* Wf, float* c,
+                      void* stream) {
+    MB_TRY(check_dtype(dt));
+    if (rows < 0) return MBERT_EINVAL;
+    if (rows > 0 && (!W || !w || !Wf || !c)) return MBERT_EINVAL;
+    if (rows == 0) return MBERT_OK;
+    return mbh::launch_fold_weight(dt, W, w, rows, Wf, c, as_stream(stream));
+}
+
+int mbert_folded_gemm(mbert_dtype dt, int kind, const void* xs, const float* stats, int total,
+                      const int32_t* meta, const void* Wf, const float* c, float eps,
+                      const float* rope, int max_positions, int table, void* out, void* stream) {
+    MB_TRY(check_dtype(dt));
+    MB_TRY(check_sizes(total, 0));
+    if (kind != MBERT_FOLD_QKV_ROPE && kind != MBERT_FOLD_GEGLU) return MBERT_EINVAL;
+    if (total > 0 && (!xs || !stats || !Wf || !c || !out)) return MBERT_EINVAL;
+    const mbh::FoldArgs fa{c, reinterpret_cast<const float2*>(stats), eps};
+    if (kind == MBERT_FOLD_QKV_ROPE) {
+        if (!meta || !rope || max_positions < 1 || (table != 0 && table != 1)) return MBERT_EINVAL;
+        return mbh::launch_qkv(dt, xs, total, meta, Wf, rope, max_positions, table, 1, out,
+                               as_stream(stream), &fa);
+    }
+    return mbh::launch_geglu(dt, xs, total, meta, Wf, out, as_stream(stream), &fa);
+}
+
 size_t mbert_pool_partial_floats(int total_max, int n_seqs) {
     if (total_max < 0 || n_seqs < 0) return 0;
     return tiles_max_for(total_max, n_seqs) * FPARTS * D;
@@ -685,13 +722,12 @@ int mbert_workspace_layout(const mbert_config* c, mbert_dtype dt, int total_max,
 }
 
 size_t mbert_folded_bytes(const mbert_config* c, mbert_dtype dt) {
-    if (check_cfg(c) || check_dtype(dt) || dt == MBERT_F16) return 0;
+    if (check_cfg(c) || check_dtype(dt)) return 0;
     return fold_layout(dt).stride * (size_t)c->n_layers;
 }
 
 int mbert_fold_norms(const mbert_weights* w, void* folded, size_t bytes, void* stream) {
     MB_TRY(check_weights(w));
-    if (w->dtype == MBERT_F16) return MBERT_EUNSUPPORTED;
     if (!folded) return MBERT_EINVAL;
     if (bytes < mbert_folded_bytes(&w->cfg, w->dtype)) return MBERT_ENOSPC;
     const FoldLayout F = fold_layout(w->dtype);

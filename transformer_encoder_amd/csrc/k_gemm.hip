@@ -860,6 +860,10 @@ int launch_fold_weight(mbert_dtype dt, const void* W, const void* w, int rows, v
             MB_LAUNCH((mb::fold_weight_kernel<mb::bf16>), grid, 256, 0, s, (const mb::bf16*)W,
                       (const mb::bf16*)w, rows, (mb::bf16*)Wf, c);
             break;
+        case MBERT_F16:
+            MB_LAUNCH((mb::fold_weight_kernel<mb::f16>), grid, 256, 0, s, (const mb::f16*)W,
+                      (const mb::f16*)w, rows, (mb::f16*)Wf, c);
+            break;
         default:
             return MBERT_EUNSUPPORTED;
     }

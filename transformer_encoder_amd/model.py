@@ -72,7 +72,7 @@ class DeviceModel:
         self.w.final_norm = B.ptr(self.final_norm)
         self.w.layers = ctypes.cast(self.layers_c, ctypes.POINTER(B.mbert_layer_weights))
         self.w.rope = B.ptr(self.rope)
-        # LayerNorms folded into the following GEMMs (bf16 and fp32; fp16 runs them apart)
+        # LayerNorms folded into the following GEMMs (every dtype; fold=False runs them apart)
         self.folded = None
         nb = B.mbert_folded_bytes(self.cfg, self.dtype)
         if fold and nb > 0:
