@@ -333,6 +333,23 @@ int mbert_encode(const mbert_weights* w, const int32_t* ids, const int32_t* cu_s
                  int n_seqs, int total, void* ws, size_t ws_bytes, float* out,
                  float* pooled, void* stream);
 
+/* mbert_encode_noalloc: mbert_encode without a caller workspace and without any allocation,
+ * for callers that cannot allocate device memory (code under stream capture, tight serving
+ * loops, harnesses that forbid hipMalloc). The workspace is a fixed device array inside the
+ * library, MBERT_NOALLOC_WORKSPACE_BYTES (64 MiB) on each GPU the library runs on, held
+ * until the process ends; its address is looked up once per device (the device current at
+ * the call; `stream` must belong to it). Returns MBERT_ENOSPC when
+ * mbert_workspace_bytes(cfg, dtype, total, n_seqs) exceeds it (about 6,000 tokens in bf16 or
+ * fp16, 3,500 in fp32), before any work is enqueued. Every part of the array is written
+ * before it is read within one call, so nothing needs clearing between calls; the array
+ * keeps the last call's contents. All calls on one GPU share the array: calls that overlap
+ * in time on one GPU (different streams or threads without ordering between them) race and
+ * corrupt each other's results. Same outputs as mbert_encode on the same inputs. */
+#define MBERT_NOALLOC_WORKSPACE_BYTES (64ull << 20)
+size_t mbert_noalloc_max_bytes(void);
+int mbert_encode_noalloc(const mbert_weights* w, const int32_t* ids, const int32_t* cu_seqlens,
+                         int n_seqs, int total, float* out, float* pooled, void* stream);
+
 /* mbert_encode_padded: padded batch ids_pad/mask [B,Tpad] on the device: unpad, encode,
  * re-pad. out_pad [B,Tpad,768] f32 with zeros at pads (the final LayerNorm writes each token's
  * row to its padded slot); pooled [B,768] (may be NULL). The packed cu_seqlens/indices stay

@@ -97,6 +97,8 @@ _SIGNATURES = {
     "mbert_workspace_layout": ([POINTER(mbert_config), I, I, I, POINTER(mbert_ws_layout)], I),
     "mbert_layer": ([POINTER(mbert_weights), I, I, I, P, SZ, P], I),
     "mbert_encode": ([POINTER(mbert_weights), P, P, I, I, P, SZ, P, P, P], I),
+    "mbert_noalloc_max_bytes": ([], SZ),
+    "mbert_encode_noalloc": ([POINTER(mbert_weights), P, P, I, I, P, P, P], I),
     "mbert_encode_padded": ([POINTER(mbert_weights), P, P, I, I, P, SZ, P, P, P], I),
     "mbert_graph_capture": ([POINTER(mbert_weights), P, P, I, I, P, SZ, P, P, P, POINTER(P)], I),
     "mbert_graph_capture_padded": ([POINTER(mbert_weights), P, P, I, I, P, SZ, P, P, P,
@@ -349,6 +351,16 @@ def mbert_fold_norms(weights, folded, nbytes, stream=None):
 def mbert_layer(weights, layer, total, n_seqs, ws, ws_bytes, stream=None):
     _call("mbert_layer", ctypes.byref(weights), layer, total, n_seqs, ptr(ws), ws_bytes,
           stream_handle(stream))
+
+
+def mbert_noalloc_max_bytes() -> int:
+    return lib().mbert_noalloc_max_bytes()
+
+
+def mbert_encode_noalloc(weights, ids, cu_seqlens, n_seqs, total, out, pooled, stream=None,
+                         check=True):
+    return _call("mbert_encode_noalloc", ctypes.byref(weights), ptr(ids), ptr(cu_seqlens), n_seqs,
+                 total, ptr(out), ptr(pooled), stream_handle(stream), check=check)
 
 
 def mbert_encode(weights, ids, cu_seqlens, n_seqs, total, ws, ws_bytes, out, pooled,

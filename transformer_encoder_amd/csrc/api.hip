@@ -3,6 +3,7 @@
 // in the kernels of k_meta / k_norm / k_gemm / k_attn.
 #include <algorithm>
 #include <climits>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -759,6 +760,50 @@ int mbert_encode(const mbert_weights* w, const int32_t* ids, const int32_t* cu, 
                  int total, void* ws, size_t ws_bytes, float* out, float* pooled, void* stream) {
     return encode_impl(w, ids, cu, n_seqs, total, ws, ws_bytes, out, pooled, as_stream(stream),
                        nullptr);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- forward without allocation
+// The workspace of mbert_encode_noalloc: a fixed device array owned by the library (one copy
+// per GPU, held until the process ends). Host code never passes this name to a kernel or a
+// copy: its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[MBERT_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MBERT_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MBERT_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MBERT_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t mbert_noalloc_max_bytes(void) { return MBERT_NOALLOC_WORKSPACE_BYTES; }
+
+int mbert_encode_noalloc(const mbert_weights* w, const int32_t* ids, const int32_t* cu,
+                         int n_seqs, int total, float* out, float* pooled, void* stream) {
+    MB_TRY(check_weights(w));
+    MB_TRY(check_sizes(total, n_seqs));
+    if (make_layout(w->dtype, total, n_seqs).total_bytes > MBERT_NOALLOC_WORKSPACE_BYTES)
+        return MBERT_ENOSPC;
+    void* ws = nullptr;
+    MB_TRY(scratch_address(&ws));
+    return encode_impl(w, ids, cu, n_seqs, total, ws, MBERT_NOALLOC_WORKSPACE_BYTES, out, pooled,
+                       as_stream(stream), nullptr);
 }
 
 int mbert_encode_padded(const mbert_weights* w, const int32_t* ids_pad, const int32_t* mask, int B,
