@@ -128,6 +128,10 @@ def lib() -> ctypes.CDLL:
         if not LIB_PATH.exists():
             raise RuntimeError(f"{LIB_PATH} is missing: build it with transformer_encoder_amd.build "
                                "(or __graft_entry__.build()); there is no fallback path")
+        # PyTorch's HIP runtime first: the library then binds to the runtime that owns the
+        # caller's device memory and streams. Loaded the other way round, the process holds
+        # two HIP runtimes and the second to initialise finds no device (hipErrorNoDevice).
+        import torch  # noqa: F401
         h = ctypes.CDLL(str(LIB_PATH))
         for name, (args, res) in _SIGNATURES.items():
             fn = getattr(h, name)

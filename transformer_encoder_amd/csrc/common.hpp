@@ -254,8 +254,11 @@ struct LaunchEvents {
 LaunchEvents& launch_events();
 }  // namespace mb
 
+// A launch first clears the thread's HIP error state, so that MB_CHECK_LAUNCH reports this
+// launch's error and not one left behind by an unrelated earlier HIP call of the caller.
 #define MB_LAUNCH(kernel, grid, block, shmem, stream, ...)                                    \
     do {                                                                                      \
+        (void)hipGetLastError();                                                              \
         ::mb::LaunchEvents& ev_ = ::mb::launch_events();                                      \
         if (ev_.stop != nullptr) {                                                            \
             hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), shmem, stream, ev_.start,  \
