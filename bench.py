@@ -37,6 +37,7 @@ PEAK_MFMA_F32 = 157.3       # TFLOP/s
 PEAK_HBM = 8000.0           # GB/s
 CALIB_BYTES = 256 << 20     # streaming calibration kernel: reads and writes this many bytes
 CALIB_NAME = "neg_kernel"
+XCDS = 8                    # accelerator complex dies, each with its own L2 and GRBM
 D, QKV, FF = 768, 2304, 1152
 GEMM_FLOPS_PER_TOKEN_LAYER = 2 * (D * QKV + D * D + D * 2 * FF + FF * D)  # 10,027,008
 
@@ -101,6 +102,7 @@ def traffic_from_profiles(kernel_kind: str, workload: str):
 
 
 GEMM_EPI = {"qkv_rope": 1, "wo_resid": 2, "wo2_resid": 2, "wi_geglu": 3}
+SUMMARY_DIR = str(ROOT / "profiles")  # where the profile summaries are written
 ROW_KERNELS = {"layernorm": "layernorm_kernel", "embed_ln": "embed_ln_kernel",
                "final_pool": "final_ln_kernel"}
 
@@ -111,7 +113,11 @@ def kernel_matches(kind: str, name: str) -> bool:
     if kind in GEMM_EPI:
         if "gemm_kernel" not in name:
             return False
-        ints = [int(x) for x in re.findall(r"Li(\d+)E", name)]
+        ints = [int(x) for x in re.findall(r"Li(\d+)E", name)]  # mangled
+        if not ints:  # demangled: gemm_kernel<type, BM, BN, NWM, NWN, EPI, ...>
+            m = re.search(r"gemm_kernel<([^>]*)>", name)
+            if m:
+                ints = [int(x) for x in m.group(1).split(",")[1:] if x.strip().lstrip("-").isdigit()]
         return len(ints) >= 5 and ints[4] == GEMM_EPI[kind]
     if kind in ROW_KERNELS:
         return ROW_KERNELS[kind] in name
@@ -154,7 +160,7 @@ def traffic_summary(fetch_dir: str, write_dir: str, kind: str, workload: str, co
            "calib_fetch_kib_raw": fc, "calib_write_kib_raw": wc,
            "fetch_scale": f_scale, "write_scale": w_scale, "dispatches": [n_f, n_w],
            "hbm_bytes_per_launch": total, "commands": commands}
-    base = ROOT / "profiles" / f"traffic_{kind}_{workload}"
+    base = Path(SUMMARY_DIR) / f"traffic_{kind}_{workload}"
     base.with_suffix(".json").write_text(json.dumps(out, indent=1) + "\n")
     md = [f"# HBM traffic per launch: {kind}, workload {workload}", "",
           "Counter runs (from the repository root on one MI355X):", "", "```", *commands, "```",
@@ -166,6 +172,183 @@ def traffic_summary(fetch_dir: str, write_dir: str, kind: str, workload: str, co
           f"- kernel sources hash: {out['source_hash']}"]
     base.with_suffix(".md").write_text("\n".join(md) + "\n")
     print(json.dumps(out))
+
+
+def classify_dispatches(names):
+    """Kernel kind of every dispatch of a trace, in dispatch order. The two residual GEMMs
+    share one symbol (attention Wo, then the MLP Wo in every layer) and so do the two
+    attention kinds (global on layers 0, 3, 6, ...): they are told apart by their order
+    within each forward, which starts at an embedding launch."""
+    kinds, n_res, n_att = [], 0, 0
+    for name in names:
+        kind = None
+        if "embed_ln_kernel" in name:
+            kind, n_res, n_att = "embed_ln", 0, 0
+        elif "attn_kernel" in name:
+            kind = "attn_global" if n_att % 3 == 0 else "attn_local"
+            n_att += 1
+        elif kernel_matches("wo_resid", name):
+            kind = "wo_resid" if n_res % 2 == 0 else "wo2_resid"
+            n_res += 1
+        else:
+            for k in ("qkv_rope", "wi_geglu", "layernorm", "final_pool"):
+                if kernel_matches(k, name):
+                    kind = k
+        kinds.append(kind)
+    return kinds
+
+
+def _trace_rows(directory: str, pattern: str):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(directory, "**", pattern), recursive=True))
+    return [(f, list(csv.DictReader(open(f)))) for f in files]
+
+
+def profile_summary(trace_dir: str, wid: int, commands: list):
+    """profiles/kernel_stats_<workload>.md from a rocprofv3 --kernel-trace --stats run with
+    CSV output: per kernel kind of the workload's process (children of the default command
+    write their own files), launches, mean duration and the achieved fraction of the
+    roofline bound, from the same algorithmic work as the bench line's roofline."""
+    from workloads import WORKLOADS, make_batch
+    wl = WORKLOADS[wid]
+    b = make_batch(wl)
+    T, lengths = int(b["cu_seqlens"][-1]), b["lengths"]
+    ds = 4 if wl.dtype == "f32" else 2
+    slots = int(b["mask"].size) if wl.layout == "padded" else T
+    best = None
+    for f, rows in _trace_rows(trace_dir, "*kernel_trace.csv"):
+        emb = [r for r in rows if "embed_ln_kernel" in r["Kernel_Name"]]
+        # the embedding launch covers 8 rows per workgroup of 256 threads
+        if emb and int(emb[0]["Grid_Size_X"]) == ((slots + 7) // 8) * 256:
+            best = (f, rows)
+    if best is None:
+        raise SystemExit(f"no trace of workload {wl.name} under {trace_dir}")
+    f, rows = best
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    # classify each stream's dispatches in its own order (the concurrency legs interleave
+    # forwards of several streams)
+    kinds = [None] * len(rows)
+    by_stream = {}
+    for i, r in enumerate(rows):
+        by_stream.setdefault(r.get("Stream_Id", "0"), []).append(i)
+    for idx in by_stream.values():
+        for i, k in zip(idx, classify_dispatches([rows[i]["Kernel_Name"] for i in idx])):
+            kinds[i] = k
+    # a launch counts when no other kernel was in flight at any time during it: launches that
+    # overlapped (the multi-stream legs) share the chip, so their durations are not its own
+    start = [int(r["Start_Timestamp"]) for r in rows]
+    end = [int(r["End_Timestamp"]) for r in rows]
+    order = sorted(range(len(rows)), key=lambda i: start[i])
+    alone = [False] * len(rows)
+    run_end = -1
+    for j, i in enumerate(order):
+        nxt = start[order[j + 1]] if j + 1 < len(order) else None
+        alone[i] = start[i] >= run_end and (nxt is None or end[i] <= nxt)
+        run_end = max(run_end, end[i])
+    per, total_ns, n_over = {}, 0.0, {}
+    for i, (r, k) in enumerate(zip(rows, kinds)):
+        d = float(end[i] - start[i])
+        if k is None:
+            k = "other: " + r["Kernel_Name"].split("(")[0][:60]
+        if not alone[i]:
+            n_over[k] = n_over.get(k, 0) + 1
+            continue
+        total_ns += d
+        per.setdefault(k, []).append(d)
+    md = [f"# Kernel times, workload {wl.name} ({wl.description}; {T} real tokens)", "",
+          "Command (from the repository root on one MI355X; the summary is written by "
+          "`bench.py --profile-summary`):", "", "```", *commands, "```", "",
+          f"Trace file: `{os.path.relpath(f, ROOT)}` (the process of this workload). Launches "
+          "that overlapped another kernel in time (the multi-stream legs: "
+          f"{sum(n_over.values())} launches) are left out; every other launch of the process is "
+          "counted.", "",
+          "| kernel kind | launches | mean us | total ms | share % | bound | achieved | of peak |",
+          "|---|---:|---:|---:|---:|---|---:|---:|"]
+    for k, ds_ in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        mean_us = sum(ds_) / len(ds_) / 1e3
+        ach = ""
+        if not k.startswith("other"):
+            bound, work, unit = kernel_work(k, T, lengths, ds)
+            if bound == "mfma":
+                a = work / (mean_us * 1e-6) / 1e12
+                pk = PEAK_MFMA_F32 if wl.dtype == "f32" else PEAK_MFMA_16BIT
+                ach = f"| mfma | {a:.0f} TFLOP/s | {a / pk:.3f}"
+            else:
+                a = work / (mean_us * 1e-6) / 1e9
+                ach = f"| hbm | {a:.0f} GB/s | {a / PEAK_HBM:.3f}"
+        else:
+            ach = "| | |"
+        md.append(f"| {k} | {len(ds_)} | {mean_us:.2f} | {sum(ds_) / 1e6:.3f} | "
+                  f"{100 * sum(ds_) / total_ns:.2f} {ach} |")
+    md += ["", "Achieved = the algorithmic work of one launch (bench.py `kernel_work`) / the mean "
+           "launch duration; peaks 2500 TFLOP/s (16-bit MFMA), 157.3 TFLOP/s (fp32 MFMA), "
+           "8000 GB/s (HBM)."]
+    out = Path(SUMMARY_DIR) / f"kernel_stats_{wl.name}.md"
+    out.write_text("\n".join(md) + "\n")
+    print(out)
+
+
+def counter_summary(dirs: list, wid: int, commands: list):
+    """profiles/counters_<workload>.md from rocprofv3 --pmc runs (one counter set per run):
+    per kernel kind, the mean per dispatch of every counter collected, and the derived MFMA
+    busy fraction, non-MFMA VALU instructions per MFMA, L2 hit rate and HBM bytes (FETCH_SIZE
+    and WRITE_SIZE scaled by what they read for the streaming calibration kernel)."""
+    from workloads import WORKLOADS
+    wl = WORKLOADS[wid]
+    vals = {}  # kind -> counter -> list
+    calib = {}
+    for d in dirs:
+        for f, rows in _trace_rows(d, "*counter_collection.csv"):
+            rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+            # one row per (dispatch, counter): classify the dispatches in order
+            disp = []
+            for r in rows:
+                if not disp or disp[-1][0] != r["Dispatch_Id"]:
+                    disp.append((r["Dispatch_Id"], r["Kernel_Name"]))
+            kinds = dict(zip([x[0] for x in disp], classify_dispatches([x[1] for x in disp])))
+            for r in rows:
+                c, v = r["Counter_Name"], float(r["Counter_Value"])
+                if CALIB_NAME in r["Kernel_Name"]:
+                    calib.setdefault(c, []).append(v)
+                k = kinds.get(r["Dispatch_Id"])
+                if k:
+                    vals.setdefault(k, {}).setdefault(c, []).append(v)
+    mean = lambda x: sum(x) / len(x)
+    simd = 256 * 4  # SIMDs on the chip
+    md = [f"# Counters per kernel kind, workload {wl.name}", "",
+          "Commands (from the repository root on one MI355X, one counter set per run; the "
+          "summary is written by `bench.py --counter-summary`):", "", "```", *commands, "```", "",
+          "Per dispatch means. MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 "
+          "SIMDs) (GRBM_GUI_ACTIVE is summed over the 8 XCDs, each with its own GPU busy counter); VALU/MFMA = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA; L2 hit = TCC_HIT / "
+          "(TCC_HIT + TCC_MISS); HBM MB = FETCH_SIZE and WRITE_SIZE (KiB) scaled by the factor "
+          f"that makes each read {CALIB_BYTES >> 20} MiB for the streaming calibration kernel "
+          "(`torch.neg` on 256 MiB).", ""]
+    fs = ws = None
+    if calib.get("FETCH_SIZE"):
+        fs = (CALIB_BYTES / 1024.0) / mean(calib["FETCH_SIZE"])
+    if calib.get("WRITE_SIZE"):
+        ws = (CALIB_BYTES / 1024.0) / mean(calib["WRITE_SIZE"])
+    md.append(f"Calibration: FETCH scale {fs if fs is None else round(fs, 4)}, "
+              f"WRITE scale {ws if ws is None else round(ws, 4)}.")
+    md += ["", "| kernel kind | dispatches | MFMA busy | VALU/MFMA | L2 hit | HBM read MB | HBM write MB | raw means |",
+           "|---|---:|---:|---:|---:|---:|---:|---|"]
+    for k, cs in sorted(vals.items()):
+        n = max(len(v) for v in cs.values())
+        g = lambda c: mean(cs[c]) if c in cs else None
+        busy = (f"{g('SQ_VALU_MFMA_BUSY_CYCLES') / (g('GRBM_GUI_ACTIVE') / XCDS * simd):.3f}"
+                if g("SQ_VALU_MFMA_BUSY_CYCLES") is not None and g("GRBM_GUI_ACTIVE") else "")
+        vpm = (f"{(g('SQ_INSTS_VALU') - g('SQ_INSTS_MFMA')) / g('SQ_INSTS_MFMA'):.2f}"
+               if g("SQ_INSTS_VALU") is not None and g("SQ_INSTS_MFMA") else "")
+        hit = (f"{g('TCC_HIT_sum') / (g('TCC_HIT_sum') + g('TCC_MISS_sum')):.3f}"
+               if g("TCC_HIT_sum") is not None and g("TCC_MISS_sum") is not None else "")
+        rd = f"{g('FETCH_SIZE') * fs * 1024 / 1e6:.1f}" if g("FETCH_SIZE") is not None and fs else ""
+        wr = f"{g('WRITE_SIZE') * ws * 1024 / 1e6:.1f}" if g("WRITE_SIZE") is not None and ws else ""
+        raw = "; ".join(f"{c} {mean(v):.4g}" for c, v in sorted(cs.items()))
+        md.append(f"| {k} | {n} | {busy} | {vpm} | {hit} | {rd} | {wr} | {raw} |")
+    out = Path(SUMMARY_DIR) / f"counters_{wl.name}.md"
+    out.write_text("\n".join(md) + "\n")
+    print(out)
 
 
 def cpu_baseline(wl, weights, batch, budget_s=12.0):
@@ -374,9 +557,25 @@ def main():
                     help="write profiles/traffic_<kind>_<workload>.{json,md} from two "
                          "rocprofv3 --pmc runs of this script and exit")
     ap.add_argument("--kind", default="wi_geglu", help="kernel kind for --traffic-summary")
+    ap.add_argument("--profile-summary", metavar="TRACE_DIR",
+                    help="write profiles/kernel_stats_<workload>.md from a rocprofv3 "
+                         "--kernel-trace --stats --output-format csv run and exit")
+    ap.add_argument("--summary-dir", help="directory for the summaries (default profiles/)")
+    ap.add_argument("--counter-summary", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/counters_<workload>.md from rocprofv3 --pmc runs and exit")
     ap.add_argument("--command", action="append", default=[],
                     help="the counter-run commands, recorded in the summary")
     args = ap.parse_args()
+    global SUMMARY_DIR
+    if args.summary_dir:
+        SUMMARY_DIR = args.summary_dir
+        os.makedirs(SUMMARY_DIR, exist_ok=True)
+    if args.profile_summary:
+        profile_summary(args.profile_summary, args.workload, args.command)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary, args.workload, args.command)
+        return
     if args.traffic_summary:
         from workloads import WORKLOADS
         traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.kind,
