@@ -15,6 +15,8 @@ launches only), and reported under `other_workloads`. Prints one JSON line.
 Per-kernel roofline: every launch of the dominant kernel (the kind with the largest share of
 one eager forward) is bracketed with HIP events on the stream it runs on, over the eager timed
 steps; achieved = algorithmic flops (or bytes) per launch / mean launch duration.
+`reference_rates` (outside every timed region): a 1 GiB streaming copy and PyTorch's GEMM on
+the projection shapes, the practical ceilings the fractions can be read against.
 """
 from __future__ import annotations
 
@@ -435,6 +437,54 @@ def measure_heads(B, m, wl, ws, rows_ptr, total_max, T, S, stream, steps):
     return res
 
 
+def measure_reference_rates(T: int, dtype: str):
+    """Rates of plain library work on the same GPU, outside every timed region: a streaming
+    copy (the practical ceiling of the HBM-bound kernels, which read and write once) and
+    PyTorch's GEMM (hipBLASLt / rocBLAS) on the forward's four projection shapes with no
+    epilogue, as a vendor-library reference for the MFMA-bound ones."""
+    import torch
+    dev = torch.device("cuda", 0)
+    res = {}
+    n = 1 << 28  # 1 GiB of fp32
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * 4 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    res["hbm_copy_gb_s"] = round(gbs, 1)
+    res["hbm_copy_frac_of_peak"] = round(gbs / PEAK_HBM, 4)
+    del src, dst
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    gemms = {}
+    for name, (K, N) in {"qkv": (768, 2304), "wo": (768, 768), "wi": (768, 2304),
+                         "wo2": (1152, 768)}.items():
+        if name == "wi":
+            continue  # same shape as qkv
+        a = torch.randn(T, K, device=dev).to(tdt)
+        b = torch.randn(K, N, device=dev).to(tdt)  # contiguous [K, N]: a plain 2-D product
+        for _ in range(3):
+            c = torch.mm(a, b)
+        e0.record()
+        for _ in range(20):
+            c = torch.mm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 20 * 1e3
+        tf = 2.0 * T * K * N / (us * 1e-6) / 1e12
+        peak = PEAK_MFMA_F32 if dtype == "f32" else PEAK_MFMA_16BIT
+        gemms[f"{name}_{T}x{K}x{N}"] = {"us": round(us, 2), "tflops": round(tf, 1),
+                                        "frac_of_peak": round(tf / peak, 4)}
+        del a, b, c
+    res["torch_mm_plain_gemm"] = gemms
+    return res
+
+
 def measure_concurrency(B, m, padded, args_in, out_like, pooled_like, ws_like, steps, warmup):
     """Throughput with G independent batches in flight on G streams (one captured forward per
     stream, each with its own workspace and outputs, launched round-robin): the rate a server
@@ -510,7 +560,8 @@ EXTRA_RUNS = {2: (100, 10), 3: (50, 5), 5: (10, 2), 4: (50, 5)}
 
 def other_workloads(headline: int) -> dict:
     """The other workloads, each measured by this script in a child process of its own (graph
-    replay, dominant-kernel roofline, no CPU baseline or head timings), keyed by name."""
+    replay, dominant-kernel roofline and reference rates, no CPU baseline or head timings),
+    keyed by name."""
     import subprocess
     from workloads import WORKLOADS
     res = {}
@@ -532,7 +583,7 @@ def other_workloads(headline: int) -> dict:
         keep = ("value", "unit", "ms_per_step", "steps", "warmup", "dtype", "mfma_peak_frac",
                 "algorithmic_tflop_per_step", "eager_ms_per_step", "graph_ms_per_step",
                 "single_stream_graph_ms_per_step", "graph_matches_eager", "roofline",
-                "kernel_ms_share")
+                "kernel_ms_share", "reference_rates")
         res[WORKLOADS[wid].name] = {"config": d["config"], **{k: d[k] for k in keep if k in d}}
     return res
 
@@ -543,6 +594,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--no-reference", action="store_true",
+                    help="skip the streaming-copy and library-GEMM reference rates")
     ap.add_argument("--no-extra", action="store_true",
                     help="measure only --workload, not the other workloads in child processes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -732,6 +785,10 @@ def main():
         for v in concurrency.values():
             v["tokens_per_s"] = round(T / (v["ms_per_step"] * 1e-3), 1)
 
+    reference_rates = None
+    if not args.no_reference:
+        reference_rates = measure_reference_rates(T, wl.dtype)
+
     keymask = None
     if padded and not args.no_heads:
         # the same padded batch run at full width with a key padding mask (no unpadding)
@@ -831,6 +888,8 @@ def main():
         line["padded_keymask"] = keymask
     if heads is not None:
         line["heads"] = heads
+    if reference_rates is not None:
+        line["reference_rates"] = reference_rates
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, weights, batch)
     if not args.no_extra:
