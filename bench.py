@@ -15,8 +15,10 @@ launches only), and reported under `other_workloads`. Prints one JSON line.
 Per-kernel roofline: every launch of the dominant kernel (the kind with the largest share of
 one eager forward) is bracketed with HIP events on the stream it runs on, over the eager timed
 steps; achieved = algorithmic flops (or bytes) per launch / mean launch duration.
-`reference_rates` (outside every timed region): a 1 GiB streaming copy and PyTorch's GEMM on
-the projection shapes, the practical ceilings the fractions can be read against.
+`reference_rates` (outside every timed region): a 1 GiB streaming copy, the library's MFMA-only
+calibration kernel (`mbert_mfma_probe`) and PyTorch's GEMM on the projection shapes, the
+practical ceilings the fractions can be read against; `roofline.measured_peak` is the copy's
+or the probe's rate for the dominant kernel's bound.
 """
 from __future__ import annotations
 
@@ -55,6 +57,15 @@ def attention_pairs(lengths, is_global, W=64):
             i = np.arange(L)
             tot += int((np.minimum(L - 1, i + W) - np.maximum(0, i - W) + 1).sum())
     return tot
+
+
+def mfma_flops(kind, T, lengths):
+    """Algorithmic matrix flops of one launch of a kernel kind (0 for the row kernels): the
+    GEMM's 2 M N K, or 4 * 64 flops per in-band (query, key) pair and head of attention."""
+    return {"qkv_rope": 2.0 * T * D * QKV, "wi_geglu": 2.0 * T * D * 2 * FF,
+            "wo_resid": 2.0 * T * D * D, "wo2_resid": 2.0 * T * FF * D,
+            "attn_global": 4.0 * 64 * 12 * attention_pairs(lengths, True),
+            "attn_local": 4.0 * 64 * 12 * attention_pairs(lengths, False)}.get(kind, 0.0)
 
 
 def kernel_work(kind, T, lengths, dtype_bytes, n_layers=22, n_global=8):
@@ -296,8 +307,11 @@ def counter_summary(dirs: list, wid: int, commands: list):
     per kernel kind, the mean per dispatch of every counter collected, and the derived MFMA
     busy fraction, non-MFMA VALU instructions per MFMA, L2 hit rate and HBM bytes (FETCH_SIZE
     and WRITE_SIZE scaled by what they read for the streaming calibration kernel)."""
-    from workloads import WORKLOADS
+    from workloads import WORKLOADS, make_batch
     wl = WORKLOADS[wid]
+    b = make_batch(wl)
+    T, lengths = int(b["cu_seqlens"][-1]), b["lengths"]
+    flops_per_mfma = 4096.0 if wl.dtype == "f32" else 32768.0  # 32x32x2 f32 / 32x32x16 16-bit
     vals = {}  # kind -> counter -> list
     calib = {}
     for d in dirs:
@@ -323,7 +337,9 @@ def counter_summary(dirs: list, wid: int, commands: list):
           "summary is written by `bench.py --counter-summary`):", "", "```", *commands, "```", "",
           "Per dispatch means. MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 "
           "SIMDs) (GRBM_GUI_ACTIVE is summed over the 8 XCDs, each with its own GPU busy counter); VALU/MFMA = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA; L2 hit = TCC_HIT / "
-          "(TCC_HIT + TCC_MISS); HBM MB = FETCH_SIZE and WRITE_SIZE (KiB) scaled by the factor "
+          "(TCC_HIT + TCC_MISS); MFMA work = SQ_INSTS_MFMA x the flops of one instruction / the "
+          "launch's algorithmic matrix flops (above 1: tile padding and masked key tiles); "
+          "HBM MB = FETCH_SIZE and WRITE_SIZE (KiB) scaled by the factor "
           f"that makes each read {CALIB_BYTES >> 20} MiB for the streaming calibration kernel "
           "(`torch.neg` on 256 MiB).", ""]
     fs = ws = None
@@ -333,8 +349,8 @@ def counter_summary(dirs: list, wid: int, commands: list):
         ws = (CALIB_BYTES / 1024.0) / mean(calib["WRITE_SIZE"])
     md.append(f"Calibration: FETCH scale {fs if fs is None else round(fs, 4)}, "
               f"WRITE scale {ws if ws is None else round(ws, 4)}.")
-    md += ["", "| kernel kind | dispatches | MFMA busy | VALU/MFMA | L2 hit | HBM read MB | HBM write MB | raw means |",
-           "|---|---:|---:|---:|---:|---:|---:|---|"]
+    md += ["", "| kernel kind | dispatches | MFMA busy | VALU/MFMA | MFMA work executed / algorithmic | L2 hit | HBM read MB | HBM write MB | raw means |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|---|"]
     for k, cs in sorted(vals.items()):
         n = max(len(v) for v in cs.values())
         g = lambda c: mean(cs[c]) if c in cs else None
@@ -346,8 +362,11 @@ def counter_summary(dirs: list, wid: int, commands: list):
                if g("TCC_HIT_sum") is not None and g("TCC_MISS_sum") is not None else "")
         rd = f"{g('FETCH_SIZE') * fs * 1024 / 1e6:.1f}" if g("FETCH_SIZE") is not None and fs else ""
         wr = f"{g('WRITE_SIZE') * ws * 1024 / 1e6:.1f}" if g("WRITE_SIZE") is not None and ws else ""
+        alg = mfma_flops(k, T, lengths)
+        ex = (f"{g('SQ_INSTS_MFMA') * flops_per_mfma / alg:.3f}"
+              if g("SQ_INSTS_MFMA") is not None and alg > 0 else "")
         raw = "; ".join(f"{c} {mean(v):.4g}" for c, v in sorted(cs.items()))
-        md.append(f"| {k} | {n} | {busy} | {vpm} | {hit} | {rd} | {wr} | {raw} |")
+        md.append(f"| {k} | {n} | {busy} | {vpm} | {ex} | {hit} | {rd} | {wr} | {raw} |")
     out = Path(SUMMARY_DIR) / f"counters_{wl.name}.md"
     out.write_text("\n".join(md) + "\n")
     print(out)
@@ -460,6 +479,23 @@ def measure_reference_rates(T: int, dtype: str):
     res["hbm_copy_gb_s"] = round(gbs, 1)
     res["hbm_copy_frac_of_peak"] = round(gbs / PEAK_HBM, 4)
     del src, dst
+    # the library's MFMA-only calibration kernel: 1024 workgroups of 4 waves (4 per SIMD)
+    from transformer_encoder_amd import binding as B
+    blocks, iters = 1024, 2000
+    probe_out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        B.mbert_mfma_probe(B.DTYPES[dtype], blocks, iters, probe_out)
+    e0.record()
+    for _ in range(5):
+        B.mbert_mfma_probe(B.DTYPES[dtype], blocks, iters, probe_out)
+    e1.record()
+    torch.cuda.synchronize()
+    flops = blocks * 4 * iters * 4 * 32768.0
+    tf = flops / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e12
+    peak = PEAK_MFMA_F32 if dtype == "f32" else PEAK_MFMA_16BIT
+    res["mfma_probe_tflops"] = round(tf, 1)
+    res["mfma_probe_frac_of_peak"] = round(tf / peak, 4)
+    del probe_out
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
     gemms = {}
     peak = PEAK_MFMA_F32 if dtype == "f32" else PEAK_MFMA_16BIT
@@ -487,6 +523,46 @@ def measure_reference_rates(T: int, dtype: str):
                                         "frac_of_peak": round(tf / peak, 4), "faster_layout": layout}
         del a, b, w
     res["torch_plain_gemm"] = gemms
+    return res
+
+
+def measure_sweep(B, m, batch, steps_small=10, steps_large=3):
+    """Throughput against batch size for a packed batch of equal-length sequences: the first
+    n sequences for n = 1, 2, 4, ... up to all of them, each forward captured as one graph
+    and replayed (tokens/s at every residency up to the full batch)."""
+    import torch
+    dev = torch.device("cuda", 0)
+    lengths = np.asarray(batch["lengths"])
+    cu_all = np.asarray(batch["cu_seqlens"])
+    res = {}
+    n = 1
+    while n <= len(lengths):
+        T = int(cu_all[n])
+        ids = torch.from_numpy(np.ascontiguousarray(batch["ids"][:T].astype(np.int32))).to(dev)
+        cu = torch.from_numpy(np.ascontiguousarray(cu_all[:n + 1].astype(np.int32))).to(dev)
+        ws = m.workspace(T, n)
+        out = torch.empty((T, D), dtype=torch.float32, device=dev)
+        pooled = torch.empty((n, D), dtype=torch.float32, device=dev)
+        st = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            g = B.mbert_graph_capture(m.w, ids, cu, n, T, ws, ws.numel(), out, pooled, st)
+        steps = steps_small if n <= 8 else steps_large
+        for _ in range(2):
+            B.mbert_graph_launch(g, st)
+        st.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(steps):
+            B.mbert_graph_launch(g, st)
+        e1.record(st)
+        st.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        B.mbert_graph_destroy(g)
+        res[str(n)] = {"tokens": T, "ms_per_step": round(ms, 4), "steps": steps,
+                       "tokens_per_s": round(T / (ms * 1e-3), 1)}
+        del ids, cu, ws, out, pooled
+        n *= 2
     return res
 
 
@@ -588,7 +664,7 @@ def other_workloads(headline: int) -> dict:
         keep = ("value", "unit", "ms_per_step", "steps", "warmup", "dtype", "mfma_peak_frac",
                 "algorithmic_tflop_per_step", "eager_ms_per_step", "graph_ms_per_step",
                 "single_stream_graph_ms_per_step", "graph_matches_eager", "roofline",
-                "kernel_ms_share", "reference_rates")
+                "kernel_ms_share", "reference_rates", "batch_sweep")
         res[WORKLOADS[wid].name] = {"config": d["config"], **{k: d[k] for k in keep if k in d}}
     return res
 
@@ -599,6 +675,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip workload 5's throughput sweep over 1, 2, 4, ... 32 sequences")
     ap.add_argument("--no-reference", action="store_true",
                     help="skip the streaming-copy and library-GEMM reference rates")
     ap.add_argument("--no-extra", action="store_true",
@@ -790,6 +868,10 @@ def main():
         for v in concurrency.values():
             v["tokens_per_s"] = round(T / (v["ms_per_step"] * 1e-3), 1)
 
+    sweep = None
+    if wl.id == 5 and not args.no_sweep:
+        sweep = measure_sweep(B, m, batch)
+
     reference_rates = None
     if not args.no_reference:
         reference_rates = measure_reference_rates(T, wl.dtype)
@@ -893,8 +975,14 @@ def main():
         line["padded_keymask"] = keymask
     if heads is not None:
         line["heads"] = heads
+    if sweep is not None:
+        line["batch_sweep"] = sweep
     if reference_rates is not None:
         line["reference_rates"] = reference_rates
+        measured = (reference_rates["mfma_probe_tflops"] if bound == "mfma"
+                    else reference_rates["hbm_copy_gb_s"])
+        line["roofline"]["measured_peak"] = measured
+        line["roofline"]["frac_of_measured_peak"] = round(achieved / measured, 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, weights, batch)
     if not args.no_extra:

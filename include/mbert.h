@@ -409,6 +409,16 @@ int mbert_graph_capture_padded_grouped(const mbert_weights* w, const int32_t* id
 int mbert_graph_launch(mbert_graph* graph, void* stream);
 int mbert_graph_destroy(mbert_graph* graph);
 
+/* Calibration (not part of the forward): the sustained dense MFMA rate of this GPU. Launches
+ * `blocks` workgroups of 4 wave64s on `stream`; every wave runs `iters` rounds of four
+ * independent 32x32 MFMA accumulations on operands held in registers (v_mfma_f32_32x32x16
+ * for bf16 / fp16, four v_mfma_f32_32x32x2_f32 per slot for fp32), 32,768 flops per slot, so
+ * the launch does blocks * 4 * iters * 4 * 32768 flops and its duration gives the rate.
+ * `out`: device floats [blocks * 256] (written; values meaningless). Asynchronous.
+ * Errors: MBERT_EINVAL for blocks outside [1, 65536], iters outside [1, 2^20] or a null
+ * `out`; MBERT_EUNSUPPORTED for another dtype. */
+int mbert_mfma_probe(mbert_dtype dtype, int blocks, int iters, float* out, void* stream);
+
 /* Kernel kinds for per-kernel timing. */
 #define MBERT_K_EMBED_LN 0
 #define MBERT_K_LAYERNORM 1

@@ -97,11 +97,13 @@ def test_counter_summary_scales_grbm_by_the_xcd_count(tmp_path, monkeypatch):
     header = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
     rows = []
     # 2 dispatches of the QKV GEMM: 1000 GPU-busy cycles per XCD (8000 summed), MFMA busy
-    # cycles = 0.25 of 1000 cycles x 1024 SIMDs
+    # cycles = 0.25 of 1000 cycles x 1024 SIMDs, exactly the algorithmic MFMA count of the
+    # 28,186-token workload (32,768 flops each), 3.5 other VALU instructions per MFMA
+    n_mfma = 2.0 * 28186 * 768 * 2304 / 32768
     for disp in (1, 2):
         rows += [[disp, QKV, "GRBM_GUI_ACTIVE", 8000.0],
                  [disp, QKV, "SQ_VALU_MFMA_BUSY_CYCLES", 0.25 * 1000 * 1024],
-                 [disp, QKV, "SQ_INSTS_MFMA", 100.0], [disp, QKV, "SQ_INSTS_VALU", 450.0]]
+                 [disp, QKV, "SQ_INSTS_MFMA", n_mfma], [disp, QKV, "SQ_INSTS_VALU", 4.5 * n_mfma]]
     d = tmp_path / "pmc"
     d.mkdir()
     _write(d / "r_counter_collection.csv", header, rows)
@@ -109,7 +111,7 @@ def test_counter_summary_scales_grbm_by_the_xcd_count(tmp_path, monkeypatch):
     md = (tmp_path / "counters_s64_loguniform32-2048_bf16.md").read_text()
     line = next(ln for ln in md.splitlines() if ln.startswith("| qkv_rope |"))
     cells = [c.strip() for c in line.split("|")]
-    assert cells[2] == "2" and cells[3] == "0.250" and cells[4] == "3.50"
+    assert cells[2] == "2" and cells[3] == "0.250" and cells[4] == "3.50" and cells[5] == "1.000"
 
 
 def test_traffic_summary_calibrates_on_the_streaming_kernel(tmp_path, monkeypatch):

@@ -157,3 +157,18 @@ def test_mbert_layer_chain_against_oracle(dtype):
     else:
         check_16bit(host(out), ref, f"{dtype} chain tokens")
         check_16bit(host(pooled), rpool, f"{dtype} chain pooled")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_mfma_probe_runs_and_is_deterministic(dtype):
+    """The MFMA calibration kernel: every workgroup computes the same accumulator sums from the
+    same register operands, so thread t of every block writes the same finite value."""
+    from transformer_encoder_amd import binding as B
+    t = torch()
+    blocks = 300
+    out = t.full((blocks * 256,), float("nan"), dtype=t.float32, device="cuda")
+    B.mbert_mfma_probe(B.DTYPES[dtype], blocks, 50, out)
+    t.cuda.synchronize()
+    o = host(out).reshape(blocks, 256)
+    assert np.all(np.isfinite(o))
+    assert np.all(o == o[0:1])

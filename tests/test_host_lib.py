@@ -161,6 +161,12 @@ def test_step_validation_paths(lib):
     assert lib.mbert_unpad(fake, fake, -1, 5, 8192, fake, fake, fake, fake, fake, None) == B.MBERT_EINVAL
     assert lib.mbert_final_ln_pool(fake, 10, fake, 1, 1, fake, 1e-5, fake, fake, None, None) == B.MBERT_EINVAL
     assert lib.mbert_graph_launch(None, None) == B.MBERT_EINVAL
+    # the MFMA calibration kernel: sizes and dtype checked before any launch
+    assert lib.mbert_mfma_probe(1, 0, 10, fake, None) == B.MBERT_EINVAL
+    assert lib.mbert_mfma_probe(1, 1 << 17, 10, fake, None) == B.MBERT_EINVAL
+    assert lib.mbert_mfma_probe(1, 256, 0, fake, None) == B.MBERT_EINVAL
+    assert lib.mbert_mfma_probe(1, 256, 10, None, None) == B.MBERT_EINVAL
+    assert lib.mbert_mfma_probe(7, 256, 10, fake, None) == B.MBERT_EUNSUPPORTED
     # pooling and heads
     assert lib.mbert_pool(fake, 10, fake, 1, 4, fake, fake, None) == B.MBERT_EINVAL
     assert lib.mbert_pool(fake, 10, None, 1, 0, fake, fake, None) == B.MBERT_EINVAL

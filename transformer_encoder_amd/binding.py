@@ -74,6 +74,7 @@ _SIGNATURES = {
     "mbert_read_status": ([P, POINTER(c_int32), P], I),
     "mbert_embed_ln": ([I, P, I, P, P, I, P, c_float, P, P, P], I),
     "mbert_layernorm": ([I, P, I, P, P, c_float, P, P], I),
+    "mbert_mfma_probe": ([I, I, I, P, P], I),
     "mbert_qkv_rope": ([I, P, I, P, P, P, I, I, I, P, P], I),
     "mbert_rope": ([I, P, I, P, P, I, I, P], I),
     "mbert_attention": ([I, P, I, P, I, I, I, P, P], I),
@@ -240,6 +241,10 @@ def mbert_read_status(meta, stream=None) -> list[int]:
 def mbert_embed_ln(dtype, ids, total, meta, tok_emb, vocab, norm_w, eps, resid, h, stream=None):
     _call("mbert_embed_ln", dtype, ptr(ids), total, ptr(meta), ptr(tok_emb), vocab, ptr(norm_w),
           eps, ptr(resid), ptr(h), stream_handle(stream))
+
+
+def mbert_mfma_probe(dtype, blocks, iters, out, stream=None):
+    _call("mbert_mfma_probe", dtype, blocks, iters, ptr(out), stream_handle(stream))
 
 
 def mbert_layernorm(dtype, x, total, meta, w, eps, y, stream=None):

@@ -489,6 +489,12 @@ int mbert_embed_ln(mbert_dtype dt, const int32_t* ids, int total, const int32_t*
                                 as_stream(stream));
 }
 
+int mbert_mfma_probe(mbert_dtype dt, int blocks, int iters, float* out, void* stream) {
+    MB_TRY(check_dtype(dt));
+    if (blocks < 1 || blocks > (1 << 16) || iters < 1 || iters > (1 << 20) || !out) return MBERT_EINVAL;
+    return mbh::launch_mfma_probe(dt, blocks, iters, out, as_stream(stream));
+}
+
 int mbert_layernorm(mbert_dtype dt, const float* x, int total, const int32_t* meta, const void* w,
                     float eps, void* y, void* stream) {
     MB_TRY(check_dtype(dt));

@@ -222,6 +222,7 @@ struct FoldArgs {
     const float2* stats;   // [rows][12] {mean, M2} per 64-column chunk
     float eps;
 };
+int launch_mfma_probe(mbert_dtype dt, int blocks, int iters, float* out, hipStream_t s);
 int launch_qkv(mbert_dtype dt, const void* h, int total, const int32_t* meta, const void* W,
                const float* rope, int max_pos, int table, int apply_rope, void* qkv,
                hipStream_t s, const FoldArgs* fold = nullptr);

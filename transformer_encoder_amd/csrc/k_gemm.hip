@@ -688,6 +688,34 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
 
 
 
+
+// Calibration of the matrix cores (not part of the forward): every wave runs `iters` rounds of
+// four independent 32x32 MFMA accumulations on operands held in registers, so the kernel's
+// duration gives the sustained dense MFMA rate of this chip for type T (16-bit: 32x32x16,
+// 32,768 flops per instruction; fp32: 32x32x2 x 4 per round slot, the same 32,768). Each
+// thread writes one float (the sum of its accumulators) so that nothing is optimised away.
+template <typename T>
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* out) {
+    const unsigned lane = threadIdx.x & 63;
+    const u32x4 a = {0x3f803f80u ^ lane, 0x3f803f80u, 0x3c003c00u, 0x3f803f80u ^ (lane << 16)};
+    const u32x4 b = {0x3c003c00u, 0x3f803f80u ^ lane, 0x3c003c00u, 0x3f803f80u};
+    f32x16 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) MfmaOp<T>::run(a, b, acc[j]);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += acc[j][e];
+    out[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 // Tile shapes, by grid size (K is 768 or 1152, so a tile lives for only 12-36 K-steps and a
 // small grid is bound by per-workgroup latency and by how evenly the tiles cover 256 CUs):
 //   256x256, 8 waves of 128x64  - many rows: twice the MFMA work per wave per K-step
@@ -743,6 +771,17 @@ int resid_t(const GemmArgs& a, hipStream_t s) {
 
 namespace mbh {
 using namespace mb;
+
+int launch_mfma_probe(mbert_dtype dt, int blocks, int iters, float* out, hipStream_t s) {
+    switch (dt) {
+        case MBERT_F32: MB_LAUNCH((mfma_probe_kernel<float>), blocks, 256, 0, s, iters, out); break;
+        case MBERT_BF16: MB_LAUNCH((mfma_probe_kernel<bf16>), blocks, 256, 0, s, iters, out); break;
+        case MBERT_F16: MB_LAUNCH((mfma_probe_kernel<f16>), blocks, 256, 0, s, iters, out); break;
+        default: return MBERT_EUNSUPPORTED;
+    }
+    MB_CHECK_LAUNCH();
+    return MBERT_OK;
+}
 
 int launch_qkv(mbert_dtype dt, const void* h, int total, const int32_t* meta, const void* W,
                const float* rope, int max_pos, int table, int apply_rope, void* qkv,
