@@ -439,7 +439,17 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
-                MB_DMA(min(kt + DS, nk - 1), kt % DS);
+                {
+                    // past the last K-step the DMA's offset lies beyond both buffer extents:
+                    // the range check drops it (no memory traffic, nothing for the epilogue
+                    // to wait for; 0.5 % per forward of 28k tokens against re-reading the
+                    // last K-step)
+                    const unsigned soff = kt + DS < nk ? (unsigned)(kt + DS) * ROWB : 0x80000000u;
+#pragma unroll
+                    for (int jg = 0; jg < GW; ++jg)
+                        lds_dma16_buf(jg < AJ ? (const void*)abase : p.B, jg < AJ ? aext : bext,
+                                      voff[jg], soff, smem + (kt % DS) * STAGE + (wu + NW * jg) * 1024);
+                }
                 MB_FRAGS(smem + ((kt + 1) % DS) * STAGE, 0, 0);
             }
             // 8 MFMAs per substep (256x256 tiles): one fragment read (and on the last substep
@@ -468,7 +478,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     }
 #undef MB_FRAGS
 #undef MB_DMA
-    // the last DMAs (re-reads of the last K-step) land before the epilogue reuses the LDS
+    // the last DMAs (dropped by the range check) complete before the epilogue reuses the LDS
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
     asm volatile("" ::: "memory");
