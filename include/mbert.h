@@ -411,9 +411,10 @@ int mbert_graph_destroy(mbert_graph* graph);
 
 /* Calibration (not part of the forward): the sustained dense MFMA rate of this GPU. Launches
  * `blocks` workgroups of 4 wave64s on `stream`; every wave runs `iters` rounds of four
- * independent 32x32 MFMA accumulations on operands held in registers (v_mfma_f32_32x32x16
- * for bf16 / fp16, four v_mfma_f32_32x32x2_f32 per slot for fp32), 32,768 flops per slot, so
- * the launch does blocks * 4 * iters * 4 * 32768 flops and its duration gives the rate.
+ * independent 32x32 MFMA accumulations on operands held in registers (one
+ * v_mfma_f32_32x32x16 per slot for bf16 / fp16: 32,768 flops; four v_mfma_f32_32x32x2_f32 per
+ * slot for fp32: 16,384 flops), so the launch does blocks * 4 * iters * 4 * (flops per slot)
+ * flops and its duration gives the rate.
  * `out`: device floats [blocks * 256] (written; values meaningless). Asynchronous.
  * Errors: MBERT_EINVAL for blocks outside [1, 65536], iters outside [1, 2^20] or a null
  * `out`; MBERT_EUNSUPPORTED for another dtype. */

@@ -701,8 +701,8 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
 
 // Calibration of the matrix cores (not part of the forward): every wave runs `iters` rounds of
 // four independent 32x32 MFMA accumulations on operands held in registers, so the kernel's
-// duration gives the sustained dense MFMA rate of this chip for type T (16-bit: 32x32x16,
-// 32,768 flops per instruction; fp32: 32x32x2 x 4 per round slot, the same 32,768). Each
+// duration gives the sustained dense MFMA rate of this chip for type T (16-bit: one 32x32x16,
+// 32,768 flops, per slot; fp32: four 32x32x2, 16,384 flops, per slot). Each
 // thread writes one float (the sum of its accumulators) so that nothing is optimised away.
 template <typename T>
 __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* out) {
