@@ -30,7 +30,8 @@
 // Epilogues that read memory issue all their loads first, from rows clamped into range, and
 // each pass issues the next pass's loads before its own stores; stores go through buffer
 // descriptors that drop rows past the end. With a folded LayerNorm (cfold / stats_in) the
-// accumulators are normalised first, rstd * (acc - mean * c); the residual epilogue can also
+// output is rstd * (acc - mean * c): the accumulators start at -mean * c (set while the first
+// operand stage lands) and the epilogue scales them by rstd; the residual epilogue can also
 // write the new residual's chunk statistics and its dtype copy for the next such GEMM.
 // Work distribution: tiles are spread over the 8 XCDs in contiguous ranges counted from the
 // real row count read on the device (the padded path sizes its grid for B * Tpad rows).
@@ -298,9 +299,11 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     constexpr int EROWS = NWM * 32;                       // rows staged per epilogue pass
     constexpr int MAIN_BYTES = DS * (BM + BN) * ROWB;
     constexpr int EPI_BYTES = EROWS * CP * 4;
-    // epilogue: the staged rows, then (folded GEMMs) {mean, rstd} per tile row and c per column
-    constexpr int EPI_ALL = EPI_BYTES + BM * 8 + BN * 4;
-    constexpr int SMEM = MAIN_BYTES > EPI_ALL ? MAIN_BYTES : EPI_ALL;
+    // folded GEMMs: mean and rstd per tile row and c per column, in LDS of their own beyond
+    // the operand stages and the epilogue staging (they are written before the main loop)
+    constexpr bool FOLDABLE = EPI == EPI_STORE || EPI == EPI_ROPE || EPI == EPI_GEGLU;
+    constexpr int FOLD_OFF = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+    constexpr int SMEM = FOLD_OFF + (FOLDABLE ? BM * 8 + BN * 4 : 0);
     static_assert(EPI != EPI_ROPE || BN % 64 == 0, "RoPE tiles hold whole heads");
     __shared__ __align__(16) unsigned char smem[SMEM];
 
@@ -336,9 +339,8 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
         for (int k = 0; k < (int)(sizeof(fbias) / sizeof(fbias[0])); ++k)
             fbias[k] = Vec4<T>::load((const T*)p.bias + bn * BN + 4 * ((tid0 + 64 * NWM * NWN * k) % S_CH));
     }
-    // Folded LayerNorm: this tile's row statistics and column sums are loaded now (they are
-    // used after the main loop, so the loads are in flight behind it)
-    constexpr bool FOLDABLE = EPI == EPI_STORE || EPI == EPI_ROPE || EPI == EPI_GEGLU;
+    // Folded LayerNorm: this tile's row statistics and column sums are loaded now, ahead of the
+    // operand DMAs, and merged while the first stage lands
     const bool fold = FOLDABLE && p.stats_in != nullptr;
     // (unconditional loads, from the weights when there is no fold, so that no branch stands
     // between them and the main loop's wait counts)
@@ -415,12 +417,61 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     // substep's MFMAs, so the previous substep's MFMAs are still in the pipe meanwhile.
 #pragma unroll
     for (int st = 0; st < DS; ++st) MB_DMA(min(st, nk - 1), st);
+    float* rmean = reinterpret_cast<float*>(smem + FOLD_OFF);  // [BM]
+    float* rrstd = rmean + BM;                                 // [BM]
+    float* cst = rrstd + BM;                                   // [BN]
+    if constexpr (FOLDABLE) {
+        if (fold) {
+            // the statistics were loaded before the DMAs: this wait leaves the DMAs in flight
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(GW * DS));
+            // Chan et al.'s pairwise merge of the 12 chunk statistics (equal counts of 64):
+            // mean = mean of the means, M2 = sum of M2 + 64 * sum of squared mean deviations;
+            // biased variance M2 / 768, eps inside the square root, as the LayerNorm kernel
+            float mean = 0.f;
+#pragma unroll
+            for (int j = 0; j < NCHUNK; ++j) mean += fst[j].x;
+            mean *= 1.0f / NCHUNK;
+            float m2 = 0.f, dev = 0.f;
+#pragma unroll
+            for (int j = 0; j < NCHUNK; ++j) {
+                m2 += fst[j].y;
+                dev += (fst[j].x - mean) * (fst[j].x - mean);
+            }
+            const float var = (m2 + 64.0f * dev) * (1.0f / D);
+            if (tid < BM) {
+                rmean[tid] = mean;
+                rrstd[tid] = 1.0f / sqrtf(var + p.eps);
+            }
+            if (tid < BN) cst[tid] = fc;
+        }
+    }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(GW * (DS - 1)));
     __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());  // also retires scalar loads, so that the
                                                  // LDS wait counts in the loop are exact
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    if constexpr (FOLDABLE) {
+        if (fold) {
+            // out = rstd * (acc - mean * c): the accumulators start at -mean * c (row mean of
+            // this lane's rows 8 (e / 4) + 4 (lane / 32) + e % 4 of each block, column sum of
+            // its column), so the epilogue only scales by rstd
+            const int rq0 = (lane >> 5) * 4;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 mv = *reinterpret_cast<const float4*>(rmean + wm * WM + 32 * i + 8 * q + rq0);
+                    const float m4[4] = {mv.x, mv.y, mv.z, mv.w};
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const float c = cst[wn * WN + 32 * j + lrow];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) acc[i][j][4 * q + t] = -m4[t] * c;
+                    }
+                }
+        }
+    }
     static_assert(SUB % 2 == 0, "fragment buffers alternate by substep");
     u32x4 af[2][FM], bf[2][FN];
     MB_FRAGS(smem, 0, 0);
@@ -541,38 +592,12 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 rpos[i][k] = min(max(rpos[i][k], 0), p.max_pos - 1);
             }
     }
-    if constexpr (FOLDABLE) {
-#pragma unroll
-        for (int j = 0; j < NCHUNK; ++j) asm volatile("" : "+v"(fst[j].x), "+v"(fst[j].y));
-        asm volatile("" : "+v"(fc));
-    }
-    float2* rowstat = reinterpret_cast<float2*>(smem + EPI_BYTES);     // [BM] {mean, rstd}
-    float* cst = reinterpret_cast<float*>(smem + EPI_BYTES + BM * 8);  // [BN]
-    if constexpr (FOLDABLE) {
-        if (fold) {
-            // Chan et al.'s pairwise merge of the 12 chunk statistics (equal counts of 64):
-            // mean = mean of the means, M2 = sum of M2 + 64 * sum of squared mean deviations;
-            // biased variance M2 / 768, eps inside the square root, as the LayerNorm kernel
-            float mean = 0.f;
-#pragma unroll
-            for (int j = 0; j < NCHUNK; ++j) mean += fst[j].x;
-            mean *= 1.0f / NCHUNK;
-            float m2 = 0.f, dev = 0.f;
-#pragma unroll
-            for (int j = 0; j < NCHUNK; ++j) {
-                m2 += fst[j].y;
-                dev += (fst[j].x - mean) * (fst[j].x - mean);
-            }
-            const float var = (m2 + 64.0f * dev) * (1.0f / D);
-            if (tid < BM) rowstat[tid] = make_float2(mean, 1.0f / sqrtf(var + p.eps));
-            if (tid < BN) cst[tid] = fc;
-        }
-    }
-    // out = rstd * (acc - mean * c) for tile row tr (0 .. BM-1) and tile column tc
+    // out = rstd * acc for tile row tr (0 .. BM-1); acc started at -mean * c
     auto fold8 = [&](float* v, int tr, int tc) {
-        const float2 st = rowstat[tr];
+        (void)tc;
+        const float r = rrstd[tr];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = (v[q] - st.x * cst[tc + q]) * st.y;
+        for (int q = 0; q < 8; ++q) v[q] *= r;
     };
     issue_loads(0);
 #pragma unroll
