@@ -260,13 +260,23 @@ def profile_summary(trace_dir: str, wid: int, commands: list):
         nxt = start[order[j + 1]] if j + 1 < len(order) else None
         alone[i] = start[i] >= run_end and (nxt is None or end[i] <= nxt)
         run_end = max(run_end, end[i])
-    per, total_ns, n_over = {}, 0.0, {}
-    for i, (r, k) in enumerate(zip(rows, kinds)):
+    # whole-batch launches only: the largest grid each kind was launched with (the grouped
+    # forward's per-group launches have smaller grids)
+    names = [k if k is not None else "other: " + r["Kernel_Name"].split("(")[0][:60]
+             for r, k in zip(rows, kinds)]
+    grid = [int(r.get("Grid_Size_X", 0) or 0) for r in rows]
+    gmax = {}
+    for i, k in enumerate(names):
+        if alone[i]:
+            gmax[k] = max(gmax.get(k, 0), grid[i])
+    per, total_ns, n_over, n_part = {}, 0.0, {}, 0
+    for i, k in enumerate(names):
         d = float(end[i] - start[i])
-        if k is None:
-            k = "other: " + r["Kernel_Name"].split("(")[0][:60]
         if not alone[i]:
             n_over[k] = n_over.get(k, 0) + 1
+            continue
+        if grid[i] != gmax[k]:
+            n_part += 1
             continue
         total_ns += d
         per.setdefault(k, []).append(d)
@@ -275,8 +285,9 @@ def profile_summary(trace_dir: str, wid: int, commands: list):
           "`bench.py --profile-summary`):", "", "```", *commands, "```", "",
           f"Trace file: `{os.path.relpath(f, ROOT)}` (the process of this workload). Launches "
           "that overlapped another kernel in time (the multi-stream legs: "
-          f"{sum(n_over.values())} launches) are left out; every other launch of the process is "
-          "counted.", "",
+          f"{sum(n_over.values())} launches) and launches on part of the batch (a smaller grid "
+          f"than the kind's largest: the grouped forward's per-group launches, {n_part}) are left "
+          "out; every other launch of the process is counted.", "",
           "| kernel kind | launches | mean us | total ms | share % | bound | achieved | of peak |",
           "|---|---:|---:|---:|---:|---|---:|---:|"]
     for k, ds_ in sorted(per.items(), key=lambda kv: -sum(kv[1])):

@@ -1,6 +1,6 @@
 """The measurement code of bench.py on synthetic rocprofv3 CSV files (CPU only): the kernel-kind
 classification of a trace, the kernel-time summary (launches that overlapped another kernel
-left out, each stream classified on its own), the counter summary (MFMA busy over
+or covered part of the batch left out, each stream classified on its own), the counter summary (MFMA busy over
 GRBM_GUI_ACTIVE summed across the 8 XCDs) and the calibrated HBM traffic."""
 import csv
 import re
@@ -71,7 +71,9 @@ def test_profile_summary_leaves_out_overlapping_launches(tmp_path, monkeypatch):
 
     # one serial forward: QKV launches of 100 ns each
     for name in forward_names():
-        launch(name, 100, grid_x=grid if name == EMBED else 1)
+        launch(name, 100, grid_x=grid if name == EMBED else 64)
+    # a launch on part of the batch (smaller grid, as a grouped forward's): left out
+    launch(QKV, 40, grid_x=16)
     # a second stream's forward overlapping a first-stream one (QKV 1000 ns, both left out)
     base = t
     for k, name in enumerate(forward_names()):
@@ -87,6 +89,7 @@ def test_profile_summary_leaves_out_overlapping_launches(tmp_path, monkeypatch):
     assert cells[2] == "4" and float(cells[3]) == pytest.approx(0.1)  # 4 launches of 100 ns
     m = re.search(r"\((\d+) launches\)|legs: (\d+) launches", md)
     assert m and int(m.group(2)) == 2 * len(forward_names())
+    assert "per-group launches, 1)" in md
     # the attention kinds of the serial forward: layers 0 and 3 global, 1 and 2 local
     g = next(ln for ln in md.splitlines() if ln.startswith("| attn_global |"))
     assert [c.strip() for c in g.split("|")][2] == "2"
