@@ -131,6 +131,9 @@ int mbert_fold_norms(const mbert_weights* w, void* folded, size_t bytes, void* s
  *   then (16-byte aligned) 4 * tiles_max ints: {q0, qn, s0, s1} per work tile: tokens
  *                          [q0, q0+qn) of the sequence [s0, s1); tiles never cross sequences;
  *                          qn <= mbert_tile_tokens()
+ *   then tiles_max ints    order: a permutation of [0, n_tiles), the order in which the
+ *                          attention takes the tiles (tiles of longer sequences first; in
+ *                          row order for the full-width padded path)
  * tiles_max = ceil(total_max / tile_tokens) + n_seqs. */
 #define MBERT_META_TOTAL 0
 #define MBERT_META_MAXLEN 1

@@ -59,6 +59,15 @@ def expected_tiles(cu, tile):
     return np.array(tiles, dtype=np.int64).reshape(-1, 4), np.array(first)
 
 
+def meta_order(meta_np, total_max, S):
+    """The attention's tile dispatch order stored after the work tiles."""
+    off = 8 + total_max + S + 1
+    off = (off + 3) & ~3
+    tiles_max = -(-total_max // 128) + S
+    n_tiles = int(meta_np[2])
+    return meta_np[off + 4 * tiles_max:off + 4 * tiles_max + n_tiles]
+
+
 def split_meta(meta_np, total_max, S):
     counts = meta_np[:8]
     pos = meta_np[8:8 + total_max]

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from gpu_util import (TOL_STEP, dev, dev_i32, expected_tiles, host, meta_for, rel_err,
-                      split_meta, torch)
+                      meta_order, split_meta, torch)
 from oracle import mbert_oracle as O
 from workloads import (WORKLOADS, cu_from_lengths, draw_lengths, make_batch, pad_batch,
                        random_matrix, rng)
@@ -49,6 +49,24 @@ def test_pack_meta_bit_exact(lengths):
     assert np.array_equal(pos, O.positions(cu))
     assert np.array_equal(first, exp_first)
     assert np.array_equal(tiles, exp_tiles)
+    check_order(meta_order(m, T, S), exp_tiles)
+
+
+def check_order(order, tiles):
+    """The attention's dispatch order: a permutation of the tiles in which the sequences'
+    key-tile counts (64 keys each, capped at 128) never increase, each sequence's tiles
+    together and in row order."""
+    assert sorted(order.tolist()) == list(range(len(tiles)))
+    if len(tiles) == 0:
+        return
+    L = tiles[order, 3] - tiles[order, 2]
+    key = np.minimum((L + 63) // 64, 128)
+    assert np.all(np.diff(key) <= 0)
+    seq = tiles[order, 2]
+    for s0 in np.unique(seq):
+        idx = np.flatnonzero(seq == s0)
+        assert np.all(np.diff(idx) == 1)                      # together
+        assert np.all(np.diff(tiles[order[idx], 0]) > 0)       # in row order
 
 
 @pytest.mark.parametrize("cu,total,bit", [([0, 5, 3], 3, 1), ([0, 4, 8], 9, 1), ([1, 4], 4, 1),
@@ -89,6 +107,7 @@ def test_unpad_bit_exact_padded_workload():
     rowmap[ref["indices"]] = np.arange(T)
     assert np.array_equal(got["rowmap"], rowmap)
     assert np.array_equal(tiles, expected_tiles(ref["cu_seqlens"], 128)[0])
+    check_order(meta_order(meta, Bn * Tp, Bn), tiles)
 
 
 def test_unpad_edges_and_holes():

@@ -80,7 +80,7 @@ def test_meta_and_workspace_layout():
         tiles_max = -(-T // 128) + S
         off = 8 + T + S + 1
         off = (off + 3) & ~3
-        assert B.mbert_meta_ints(T, S) == off + 4 * tiles_max
+        assert B.mbert_meta_ints(T, S) == off + 5 * tiles_max  # tiles, then their order
         assert B.mbert_pool_partial_floats(T, S) == tiles_max * 4 * 768  # 4 partials per tile
         for dt, ds in ((B.MBERT_F32, 4), (B.MBERT_BF16, 2), (B.MBERT_F16, 2)):
             L = B.mbert_workspace_layout(c, dt, T, S)

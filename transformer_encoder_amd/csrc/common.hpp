@@ -147,6 +147,7 @@ struct MetaView {
     int* seq_tile0;
     int4* tiles;
     int* pos;
+    int* order;  // the attention's dispatch order of the tiles (a permutation of [0, n_tiles))
 };
 __host__ __device__ inline size_t tiles_max_for(int total_max, int n_seqs) {
     return (size_t)((total_max + TILE - 1) / TILE) + (size_t)n_seqs;
@@ -159,12 +160,13 @@ __host__ __device__ inline MetaView meta_view(int* meta, int total_max, int n_se
     size_t off = 8 + (size_t)total_max + (size_t)n_seqs + 1;
     off = (off + 3) & ~(size_t)3;  // 16-byte alignment for int4 tiles
     v.tiles = reinterpret_cast<int4*>(meta + off);
+    v.order = meta + off + 4 * tiles_max_for(total_max, n_seqs);
     return v;
 }
 __host__ __device__ inline size_t meta_ints(int total_max, int n_seqs) {
     size_t off = 8 + (size_t)total_max + (size_t)n_seqs + 1;
     off = (off + 3) & ~(size_t)3;
-    return off + 4 * tiles_max_for(total_max, n_seqs);
+    return off + 5 * tiles_max_for(total_max, n_seqs);
 }
 
 // Rows to process: the device count when a meta buffer is given, else the host count.

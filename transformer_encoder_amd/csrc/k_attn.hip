@@ -119,7 +119,13 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(
     if (local >= per) return;
     const int lin = (blockIdx.x % NXCD) * per + local;
     if (lin >= n_act) return;
-    const int head = lin / n_tiles, tile = lin % n_tiles;
+    // On global layers whose grid takes more than one round of workgroup slots (3 per CU),
+    // the tiles of each head in the meta block's dispatch order (longer sequences first), so
+    // that the longest workgroups do not start last (a 64-sequence batch of 32-2048 tokens:
+    // 3-5 % faster). Local tiles all cost about the same, and a grid that fits at once does not
+    // wait for late starters: both keep the row order, which measured 1-5 % better for them.
+    const int head = lin / n_tiles;
+    const int tile = (is_global && n_act > 3 * 256) ? mv.order[lin % n_tiles] : lin % n_tiles;
     const int4 tl = mv.tiles[tile];
     const int q0 = tl.x, qn = tl.y, s0 = tl.z, s1 = tl.w;
 

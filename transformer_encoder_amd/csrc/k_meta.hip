@@ -74,6 +74,38 @@ __device__ void build_tiles(const int* cu, int S, bool ok, MetaView mv, int* lds
         mv.seq_tile0[S] = carry;
         mv.counts[MBERT_META_NTILES] = carry;
     }
+    // The attention's dispatch order: the tiles of longer sequences first (a global layer's
+    // tile costs its sequence's length in key tiles), so that the longest workgroups do not
+    // start last. A counting sort of the sequences by key tiles (64 keys each, capped at 128):
+    // tile counts per key, start offsets in descending key order, then each sequence claims
+    // its slots; within one key the order is whatever the atomics give (each tile's output is
+    // its own, so the results do not depend on it).
+    constexpr int KB = 129;
+    __shared__ int bins[KB];
+    for (int k = threadIdx.x; k < KB; k += blockDim.x) bins[k] = 0;
+    __syncthreads();
+    auto key_of = [](int L) { return min((L + 63) / 64, KB - 1); };
+    for (int s = threadIdx.x; ok && s < S; s += blockDim.x) {
+        const int L = cu[s + 1] - cu[s];
+        if (L > 0) atomicAdd(&bins[key_of(L)], (L + TILE - 1) / TILE);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int k = KB - 1; k >= 0; --k) {
+            const int c = bins[k];
+            bins[k] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    for (int s = threadIdx.x; ok && s < S; s += blockDim.x) {
+        const int L = cu[s + 1] - cu[s];
+        if (L <= 0) continue;
+        const int nt = (L + TILE - 1) / TILE;
+        const int p = atomicAdd(&bins[key_of(L)], nt), t0 = mv.seq_tile0[s];
+        for (int j = 0; j < nt; ++j) mv.order[p + j] = t0 + j;
+    }
 }
 
 // Packed path: validate cu_seqlens, then counts and tiles. One workgroup of 1024 threads.
@@ -141,9 +173,11 @@ __global__ __launch_bounds__(1024) void padded_meta_kernel(const int* __restrict
         for (int o = 32; o > 0; o >>= 1) any_after |= __shfl_xor(any_after, o, 64);
         if (any_after) status |= MBERT_STATUS_BAD_MASK;
         const int L = first;
-        for (int k = lane; k < nt; k += 64)
+        for (int k = lane; k < nt; k += 64) {
             mv.tiles[b * nt + k] = make_int4(b * Tpad + TILE * k, min(TILE, Tpad - TILE * k),
                                              b * Tpad, b * Tpad + L);
+            mv.order[b * nt + k] = b * nt + k;  // every row is Tpad queries: in row order
+        }
         if (lane == 0) mv.seq_tile0[b] = too_long ? 0 : b * nt;
     }
     if (status) atomicOr(&s_status, status);
