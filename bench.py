@@ -144,19 +144,25 @@ def traffic_summary(fetch_dir: str, write_dir: str, kind: str, workload: str, co
     CALIB_BYTES for the streaming calibration kernel of the same run."""
     import csv
     import glob
-    if kind in ("wo_resid", "wo2_resid"):
-        raise SystemExit("the two residual GEMMs share one kernel symbol; no per-kind counters")
 
     def per_dispatch(d, counter):
         f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
         if not f:
             raise SystemExit(f"no counter_collection.csv under {d}")
+        rows = sorted(csv.DictReader(open(f[0])), key=lambda r: int(r["Dispatch_Id"]))
+        # kinds that share a kernel symbol (the two residual GEMMs, global and local
+        # attention) are told apart by their order within each forward
+        disp = []
+        for r in rows:
+            if not disp or disp[-1][0] != r["Dispatch_Id"]:
+                disp.append((r["Dispatch_Id"], r["Kernel_Name"]))
+        kinds = dict(zip([x[0] for x in disp], classify_dispatches([x[1] for x in disp])))
         k_vals, c_vals = [], []
-        for r in csv.DictReader(open(f[0])):
+        for r in rows:
             if r["Counter_Name"] != counter:
                 continue
             v = float(r["Counter_Value"])
-            if kernel_matches(kind, r["Kernel_Name"]):
+            if kinds.get(r["Dispatch_Id"]) == kind:
                 k_vals.append(v)
             elif CALIB_NAME in r["Kernel_Name"]:
                 c_vals.append(v)

@@ -126,9 +126,11 @@ def test_traffic_summary_calibrates_on_the_streaming_kernel(tmp_path, monkeypatc
                                              ("WRITE_SIZE", kib, 300.0)):
         d = tmp_path / counter
         d.mkdir()
-        _write(d / "r_counter_collection.csv", header,
-               [[1, QKV, counter, kernel_read], [2, calib, counter, calib_read],
-                [3, QKV, counter, kernel_read]])
+        # two forwards' worth of the kinds around the QKV dispatches, which alone are counted
+        rows = [[1, EMBED, counter, 5.0], [2, QKV, counter, kernel_read],
+                [3, ATTN, counter, 7.0], [4, calib, counter, calib_read],
+                [5, EMBED, counter, 5.0], [6, QKV, counter, kernel_read]]
+        _write(d / "r_counter_collection.csv", header, rows)
     bench.traffic_summary(str(tmp_path / "FETCH_SIZE"), str(tmp_path / "WRITE_SIZE"), "qkv_rope",
                           "w", ["cmd"])
     import json
@@ -136,3 +138,9 @@ def test_traffic_summary_calibrates_on_the_streaming_kernel(tmp_path, monkeypatc
     # the fetch counter reads half the calibration bytes: scale 2; the write counter all: 1
     assert out["fetch_scale"] == pytest.approx(2.0) and out["write_scale"] == pytest.approx(1.0)
     assert out["hbm_bytes_per_launch"] == pytest.approx((2 * 1000.0 + 300.0) * 1024)
+    # global attention shares its symbol with local attention: classified by its order
+    bench.traffic_summary(str(tmp_path / "FETCH_SIZE"), str(tmp_path / "WRITE_SIZE"), "attn_global",
+                          "w", ["cmd"])
+    out = json.loads((tmp_path / "traffic_attn_global_w.json").read_text())
+    assert out["dispatches"] == [1, 1]
+    assert out["hbm_bytes_per_launch"] == pytest.approx((2 * 7.0 + 7.0) * 1024)
