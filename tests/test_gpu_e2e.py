@@ -134,7 +134,7 @@ def test_w5_32x8192_fp16():
 
 @pytest.mark.parametrize("fold", [True, False], ids=["folded", "separate"])
 @pytest.mark.parametrize("lengths", [[1], [1, 2, 3], [65, 0, 129], [64, 65, 300, 7]])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_edge_batches_two_layers(lengths, dtype, fold):
     from transformer_encoder_amd.model import DeviceModel
     w = make_weights(Dims(n_layers=2), dtype, 500 + len(lengths))
