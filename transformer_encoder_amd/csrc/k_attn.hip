@@ -5,8 +5,9 @@
 // attention").
 //
 // Work: one workgroup per (work tile of <= 128 query rows of one sequence, head); 4 wave64s,
-// 32 query rows each. K/V tiles of 64 keys stream through two LDS stages (prefetched into
-// registers one tile ahead, with unconditional loads). The workgroup walks only the keys its
+// 32 query rows each. K/V tiles of 64 keys stream through two LDS stages, one tile ahead: the
+// 16-bit types load them from global memory straight into the stage (buffer loads into LDS),
+// fp32 through registers, with unconditional loads. The workgroup walks only the keys its
 // band can reach: the whole sequence on a global layer, [q0 - W, q0 + qn - 1 + W] on a local
 // one; a wave whose own band misses a key tile skips its MFMAs for it. On a grid of at most
 // one workgroup per CU (16-bit types), the workgroup has 8 waves: the second four take the
@@ -22,13 +23,15 @@
 // follow the same key permutation (lane group g holds keys 4g..4g+3 and 8+4g..8+4g+3 of each
 // 16-key slice), which leaves the product unchanged.
 // Softmax is online in fp32 with exp2 and the scale 0.125 * log2(e) folded into one FMA; edge
-// tiles are masked branch-free; the running max is only raised (and the output rescaled) when a
-// row's max grows by more than 2^8.
+// tiles are masked branch-free (a per-lane bit mask of the allowed keys); the running max is only
+// raised (and the output rescaled) when a row's max grows by more than 2^8, and only then are
+// the two half-row maxima of a query (lanes l and l ^ 32) exchanged.
 // The fp32 variant uses v_mfma_f32_32x32x2_f32 and padded natural K and V rows.
 #include "common.hpp"
 
-// K/V tiles held in registers ahead of the LDS stage. One: a second stage gained 2-3 % on
-// 8192-key global layers and lost as much on short sequences.
+// fp32: K/V tiles held in registers ahead of the LDS stage (with register staging for every
+// type, a second register stage gained 2-3 % on 8192-key global layers and lost as much on
+// short sequences).
 #ifndef MB_ATTN_PREFETCH
 #define MB_ATTN_PREFETCH 1
 #endif
@@ -219,6 +222,54 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(
         }
     };
 
+    // 16-bit types: the step's K/V tiles go from global memory straight into the LDS stage
+    // (buffer loads into LDS, 16 bytes a lane, 1 KB a wave instruction), with no register
+    // staging and no LDS stores (8192-token global layer 253 -> 241 us together with the
+    // masking and max exchange below). A step holds 16 KS groups of 1 KB (per key tile 8 of
+    // K, then 8 of V; group j = rows 8j .. 8j+7); wave w fills groups w, w + NWV, ...: lane L
+    // row 8j + L / 8 at physical chunk L % 8, which holds the logical chunk that kchunk /
+    // vchunk place there (both swizzles are their own inverses). Rows past the last key
+    // re-read it, like the register path. One buffer descriptor per key tile, based at its
+    // first key, so offsets stay small for any sequence length.
+    constexpr int NWV = 4 * KS, GPW = 16 * KS / NWV;
+    static_assert(F32 || sizeof(Ks[0]) == sizeof(Vs[0]), "K and V stages of one size");
+    constexpr unsigned SSTR = (unsigned)sizeof(Ks[0]);  // bytes between stages
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    int drow[GPW];
+    unsigned dcol[GPW];
+    unsigned char* dst0[GPW];  // stage-0 destination of each group (wave-uniform)
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        const int hh = (NWV * i) / 16, within = wv + NWV * i - 16 * hh, j = within % 8;
+        const bool isv = within >= 8;
+        const int r = 8 * j + (lane >> 3), pc = lane & 7;
+        const int c = isv ? (pc ^ (((r >> 1) & 1) << 2)) : (pc ^ ((r >> 1) & 7));
+        drow[i] = r;
+        dcol[i] = (unsigned)(((isv ? 2 * D : D) + head * HD + 8 * c) * (int)sizeof(T));
+        dst0[i] = (isv ? reinterpret_cast<unsigned char*>(&Vs[0][hh][0])
+                       : reinterpret_cast<unsigned char*>(&Ks[0][hh][0])) + 1024 * j;
+    }
+    auto dma = [&](int step, int st) {
+#pragma unroll
+        for (int i = 0; i < GPW; ++i) {
+            const int hh = (NWV * i) / 16;
+            const int kbs = klo + 64 * min(KS * step + hh, nkt - 1);
+            const unsigned voff =
+                (unsigned)min(drow[i], khi - kbs) * (unsigned)(QKV * sizeof(T)) + dcol[i];
+            lds_dma16_buf(qkv + (size_t)kbs * QKV, 64u * QKV * (unsigned)sizeof(T), voff, 0u,
+                          dst0[i] + st * SSTR);
+        }
+    };
+    // the step's DMAs of this wave landed and its LDS reads are done, then the barrier: the
+    // stage just filled is visible to all, the one just read may be refilled
+    auto publish = [&]() {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
     f32x16 oacc[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -231,16 +282,22 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(
     // branch leave the wait-count pass unsure of what is in flight. Step i's tiles are held in
     // register slot i % AP; the loop is unrolled AP times so the slots are static.
     const int nst = (nkt + KS - 1) / KS;  // steps of KS key tiles
+    if constexpr (F32) {
 #pragma unroll
-    for (int u = 0; u < AP; ++u) gload(u, u);
-    sstore(0, 0);
-    __syncthreads();
+        for (int u = 0; u < AP; ++u) gload(u, u);
+        sstore(0, 0);
+        __syncthreads();
+    } else {
+        dma(0, 0);
+        publish();
+    }
     for (int it0 = 0; it0 < nst; it0 += AP) {
 #pragma unroll
     for (int u = 0; u < AP; ++u) {
         const int it = it0 + u;
         if (it >= nst) break;  // uniform over the workgroup
-        gload(it + AP, u);
+        if constexpr (F32) gload(it + AP, u);
+        else dma(it + 1, (it + 1) & 1);  // the stage read in the previous step
         const int t = KS * it + kh;  // this wave's key tile
         const int kb = klo + 64 * t;
         const bool active = t < nkt && qcnt > 0 && kb <= whi && kb + 63 >= wlo;
@@ -273,14 +330,28 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(
             float sv[32];
             float mx = -INFINITY;
             if (need_mask) {
-                // key of element e = kb + 4g + [32kk + 8(e/4) + (e%4)]; compare the constant part
+                // key of element e = kb + 4g + [32kk + 8(e/4) + (e%4)]: the allowed keys, relative
+                // to kb + 4g, are lo_rel .. hi_rel; as bits of one word per 32-key block, each
+                // element's bit sign-extended to a select mask (two VALU operations an element,
+                // no compare results in SGPRs)
                 const int lo_rel = qlo - (kb + 4 * g), hi_rel = qhi - (kb + 4 * g);
+                unsigned wbits[2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int lo = max(lo_rel - 32 * kk, 0), hi = min(hi_rel - 32 * kk, 31);
+                    wbits[kk] = hi >= lo ? (0xffffffffu >> (31 - (hi - lo))) << lo : 0u;
+                }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
-                        const int rel = 32 * kk + 8 * (e >> 2) + (e & 3);
-                        const float x = (rel >= lo_rel && rel <= hi_rel) ? sacc[kk][e] : -INFINITY;
+                        const int rel = 8 * (e >> 2) + (e & 3);
+                        const unsigned m = (unsigned)((int)(wbits[kk] << (31 - rel)) >> 31);
+                        // through a scalar: a bit cast of the vector element itself reads
+                        // element 0 with this compiler
+                        const float sval = sacc[kk][e];
+                        const float x = __builtin_bit_cast(
+                            float, (__builtin_bit_cast(unsigned, sval) & m) | (~m & 0xff800000u));
                         sv[16 * kk + e] = x;
                         mx = fmaxf(mx, x);
                     }
@@ -293,11 +364,15 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(
                         mx = fmaxf(mx, sacc[kk][e]);
                     }
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;  // row max, log2 units
+            mx *= scale_log2;  // this lane's half of the row, log2 units
             // Lazy rescale: the running max only moves (and O, l are rescaled) when some lane's
-            // row max exceeds it by more than 8; otherwise exp2 arguments stay <= 8 (p <= 256).
-            // Softmax is invariant to the subtracted constant, so the result is the same.
+            // max exceeds it by more than 8; otherwise exp2 arguments stay <= 8 (p <= 256).
+            // Softmax is invariant to the subtracted constant, so the result is the same. The
+            // two halves of a query's row (lanes l and l ^ 32) share m_run: it only moves to
+            // the maximum over both, exchanged here (8192-token global layer: 1-3 % against an
+            // exchange on every tile).
             if (__any(mx > m_run + 8.0f)) {
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
                 const float m_new = fmaxf(m_run, mx);
                 const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
                 l_run *= alpha;
@@ -356,8 +431,12 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(
                         }
             }
         }
-        if (it + 1 < nst) sstore((it + 1) & 1, (u + 1) % AP);
-        __syncthreads();
+        if constexpr (F32) {
+            if (it + 1 < nst) sstore((it + 1) & 1, (u + 1) % AP);
+            __syncthreads();
+        } else {
+            publish();
+        }
     }
     }
 

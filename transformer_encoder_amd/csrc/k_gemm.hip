@@ -135,13 +135,6 @@ template <> struct MfmaOp<float> {
     }
 };
 
-// s_waitcnt immediates (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
-// wait until at most n vector-memory operations are outstanding / until LDS operations drain.
-constexpr unsigned vmcnt_imm(int n) {
-    return (unsigned)(n & 15) | ((unsigned)((n >> 4) & 3) << 14) | (7u << 4) | (15u << 8);
-}
-constexpr unsigned lgkmcnt0_imm() { return 63u | (3u << 14) | (7u << 4); }
-
 // Barrier for LDS reuse only: waits for this wave's LDS operations, not for its global stores
 // (__syncthreads would also wait for every store in flight, serialising the epilogue passes).
 __device__ __forceinline__ void lds_barrier() {
@@ -149,21 +142,6 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-}
-
-// 16 bytes per lane from global memory straight into LDS through a buffer load (MUBUF, offset
-// = voff + soff from an SGPR base): lane i's bytes land at lds + 16 i (lds is the same for the
-// whole wave). A buffer load, not a global (FLAT) one: after a FLAT load into LDS the compiler
-// waits for every LDS operation before any use, with this one its LDS wait counts stay exact.
-// The builtin exists only for the device target; the host pass, which never runs this, would
-// otherwise drop every kernel that uses it.
-__device__ __forceinline__ void lds_dma16_buf(const void* base, unsigned extent, unsigned voff,
-                                              unsigned soff, unsigned char* lds) {
-#if __HIP_DEVICE_COMPILE__
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, extent, 0x00020000),
-        (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
-#endif
 }
 
 // The erf form of GELU, z * Phi(z) with Phi(z) = (1 + erf(z / sqrt 2)) / 2 (candding, §"The
