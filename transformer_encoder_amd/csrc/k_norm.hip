@@ -172,12 +172,15 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
 // full width) are written as zeros and left out of the sums.
 // With `scatter`, packed row k is written to row scatter[k] of `out` (the padded output), and
 // the workgroups after the LayerNorm ones write zeros to every row whose rowmap entry is
-// negative (the pads): the re-pad is part of this launch. There a wave takes 64 consecutive
+// negative (the pads): the re-pad is part of this launch. There a wave takes ZSLOTS consecutive
 // slots, reads their rowmap entries with one load and zeroes the pad rows among them, so no
-// wave waits on more than one load.
+// wave waits on more than one load. 16 slots a wave spread the zeroing of a 4096-slot batch
+// over 16 workgroups: with 64 (4 workgroups of 16 waves) the stores of the few CUs that held
+// them set the launch's time (9.5 -> 19.5 us).
 constexpr int FROWS = TILE / FPARTS;    // rows per workgroup
 constexpr int FWAVES = 16;
 constexpr int FRW = FROWS / FWAVES;     // rows per wave
+constexpr int ZSLOTS = 16;              // padded-output slots a wave checks for pad rows
 
 template <typename T>
 __global__ __launch_bounds__(64 * FWAVES) void final_ln_kernel(const float* __restrict__ resid,
@@ -193,9 +196,10 @@ __global__ __launch_bounds__(64 * FWAVES) void final_ln_kernel(const float* __re
     __shared__ float red[FWAVES][D];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if ((int)blockIdx.x >= ln_blocks) {  // pad rows of the padded output
-        const int r0 = (((int)blockIdx.x - ln_blocks) * FWAVES + wave) * 64;
+        const int r0 = (((int)blockIdx.x - ln_blocks) * FWAVES + wave) * ZSLOTS;
         if (r0 >= n_slots) return;
-        unsigned long long pads = __ballot(r0 + lane < n_slots && rowmap[r0 + lane] < 0);
+        unsigned long long pads =
+            __ballot(lane < ZSLOTS && r0 + lane < n_slots && rowmap[r0 + lane] < 0);
         const float z[12] = {};
         while (pads) {  // wave-uniform
             const int j = __builtin_ctzll(pads);
@@ -464,8 +468,9 @@ int launch_final_ln_pool(const float* resid, int total, const int32_t* meta, int
                          const int32_t* rowmap, int n_slots) {
     const size_t tmax = tiles_max_for(total, n_seqs);
     const int ln_blocks = (int)tmax * FPARTS;
-    // pad rows of the padded output: a wave per 64 slots
-    const int zero_blocks = (scatter && n_slots > 0) ? (n_slots + 64 * FWAVES - 1) / (64 * FWAVES) : 0;
+    // pad rows of the padded output: a wave per ZSLOTS slots
+    const int zero_blocks =
+        (scatter && n_slots > 0) ? (n_slots + ZSLOTS * FWAVES - 1) / (ZSLOTS * FWAVES) : 0;
     const unsigned grid = (unsigned)(ln_blocks + zero_blocks);
     if (grid > 0) {
         float* part = pooled ? partials : nullptr;
