@@ -168,7 +168,7 @@ bool use_fold(const mbert_weights* w) { return w->folded != nullptr; }
 // statistics, which the next GEMM normalises in its epilogue. Layer 0's QKV reads the
 // embedding norm output (no attention norm there); the last MLP residual feeds the final norm.
 int run_layer_folded(const mbert_weights* w, int layer, int total, int n_seqs, char* ws,
-                     const mbert_ws_layout& L, hipStream_t s, Recorder* rec) {
+                     const mbert_ws_layout& L, hipStream_t s, Recorder* rec, bool host_rows) {
     const mbert_config& c = w->cfg;
     const mbert_layer_weights& lw = w->layers[layer];
     const mbert_dtype dt = w->dtype;
@@ -185,29 +185,33 @@ int run_layer_folded(const mbert_weights* w, int layer, int total, int n_seqs, c
     if (layer == 0) {
         MB_TIMED(rec, MBERT_K_QKV_ROPE, s,
                  mbh::launch_qkv(dt, h, total, meta, lw.Wqkv, w->rope, c.max_positions, glob ? 0 : 1,
-                                 1, qkv, s));
+                                 1, qkv, s, nullptr, host_rows));
     } else {
         const mbh::FoldArgs fa{reinterpret_cast<const float*>(fb + F.cq), st, c.norm_eps};
         MB_TIMED(rec, MBERT_K_QKV_ROPE, s,
                  mbh::launch_qkv(dt, xa, total, meta, fb + F.wq, w->rope, c.max_positions,
-                                 glob ? 0 : 1, 1, qkv, s, &fa));
+                                 glob ? 0 : 1, 1, qkv, s, &fa, host_rows));
     }
     MB_TIMED(rec, glob ? MBERT_K_ATTN_GLOBAL : MBERT_K_ATTN_LOCAL, s,
              mbh::launch_attention(dt, qkv, total, meta, n_seqs, glob ? 1 : 0, c.half_window, h, s));
     MB_TIMED(rec, MBERT_K_WO_RESID, s,
-             mbh::launch_linear_residual(dt, h, D, total, meta, lw.attn_Wo, resid, s, xs, st));
+             mbh::launch_linear_residual(dt, h, D, total, meta, lw.attn_Wo, resid, s, xs, st,
+                                         host_rows));
     const mbh::FoldArgs fm{reinterpret_cast<const float*>(fb + F.ci), st, c.norm_eps};
-    MB_TIMED(rec, MBERT_K_WI_GEGLU, s, mbh::launch_geglu(dt, xa, total, meta, fb + F.wi, qkv, s, &fm));
+    MB_TIMED(rec, MBERT_K_WI_GEGLU, s,
+             mbh::launch_geglu(dt, xa, total, meta, fb + F.wi, qkv, s, &fm, host_rows));
     const bool last = layer + 1 == c.n_layers;
     MB_TIMED(rec, MBERT_K_WO2_RESID, s,
              mbh::launch_linear_residual(dt, qkv, FF, total, meta, lw.mlp_Wo, resid, s,
-                                         last ? nullptr : xs, last ? nullptr : st));
+                                         last ? nullptr : xs, last ? nullptr : st, host_rows));
     return MBERT_OK;
 }
 
+// host_rows: total is the exact row count (a packed batch), so the GEMMs need not load it.
 int run_layer(const mbert_weights* w, int layer, int total, int n_seqs, char* ws,
-              const mbert_ws_layout& L, hipStream_t s, Recorder* rec, bool fold = false) {
-    if (fold) return run_layer_folded(w, layer, total, n_seqs, ws, L, s, rec);
+              const mbert_ws_layout& L, hipStream_t s, Recorder* rec, bool fold = false,
+              bool host_rows = false) {
+    if (fold) return run_layer_folded(w, layer, total, n_seqs, ws, L, s, rec, host_rows);
     const mbert_config& c = w->cfg;
     const mbert_layer_weights& lw = w->layers[layer];
     const mbert_dtype dt = w->dtype;
@@ -221,16 +225,19 @@ int run_layer(const mbert_weights* w, int layer, int total, int n_seqs, char* ws
                  mbh::launch_layernorm(dt, resid, total, meta, lw.attn_norm, c.norm_eps, h, s));
     MB_TIMED(rec, MBERT_K_QKV_ROPE, s,
              mbh::launch_qkv(dt, h, total, meta, lw.Wqkv, w->rope, c.max_positions, glob ? 0 : 1, 1,
-                             qkv, s));
+                             qkv, s, nullptr, host_rows));
     MB_TIMED(rec, glob ? MBERT_K_ATTN_GLOBAL : MBERT_K_ATTN_LOCAL, s,
              mbh::launch_attention(dt, qkv, total, meta, n_seqs, glob ? 1 : 0, c.half_window, h, s));
     MB_TIMED(rec, MBERT_K_WO_RESID, s,
-             mbh::launch_linear_residual(dt, h, D, total, meta, lw.attn_Wo, resid, s));
+             mbh::launch_linear_residual(dt, h, D, total, meta, lw.attn_Wo, resid, s, nullptr,
+                                         nullptr, host_rows));
     MB_TIMED(rec, MBERT_K_LAYERNORM, s,
              mbh::launch_layernorm(dt, resid, total, meta, lw.mlp_norm, c.norm_eps, h, s));
-    MB_TIMED(rec, MBERT_K_WI_GEGLU, s, mbh::launch_geglu(dt, h, total, meta, lw.Wi, qkv, s));
+    MB_TIMED(rec, MBERT_K_WI_GEGLU, s,
+             mbh::launch_geglu(dt, h, total, meta, lw.Wi, qkv, s, nullptr, host_rows));
     MB_TIMED(rec, MBERT_K_WO2_RESID, s,
-             mbh::launch_linear_residual(dt, qkv, FF, total, meta, lw.mlp_Wo, resid, s));
+             mbh::launch_linear_residual(dt, qkv, FF, total, meta, lw.mlp_Wo, resid, s, nullptr,
+                                         nullptr, host_rows));
     return MBERT_OK;
 }
 
@@ -258,7 +265,7 @@ int encode_impl(const mbert_weights* w, const int32_t* ids, const int32_t* cu, i
              mbh::launch_embed_ln(w->dtype, ids, total, meta, w->tok_emb, w->cfg.vocab,
                                   w->emb_norm, w->cfg.norm_eps, resid, base + L.h, s));
     for (int l = 0; l < w->cfg.n_layers; ++l)
-        MB_TRY(run_layer(w, l, total, n_seqs, base, L, s, rec, use_fold(w)));
+        MB_TRY(run_layer(w, l, total, n_seqs, base, L, s, rec, use_fold(w), true));
     MB_TIMED(rec, MBERT_K_FINAL_POOL, s,
              mbh::launch_final_ln_pool(resid, total, meta, n_seqs, w->dtype, w->final_norm,
                                        w->cfg.norm_eps, out, pooled,

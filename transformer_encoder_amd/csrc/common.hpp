@@ -248,9 +248,12 @@ struct FoldArgs {
     float eps;
 };
 int launch_mfma_probe(mbert_dtype dt, int blocks, int iters, float* out, hipStream_t s);
+// GEMM launches take their row count from meta's device count unless host_rows is set: then
+// total is exact (a packed batch, whose meta count is total itself) and the kernels start
+// without loading the count first.
 int launch_qkv(mbert_dtype dt, const void* h, int total, const int32_t* meta, const void* W,
                const float* rope, int max_pos, int table, int apply_rope, void* qkv,
-               hipStream_t s, const FoldArgs* fold = nullptr);
+               hipStream_t s, const FoldArgs* fold = nullptr, bool host_rows = false);
 // Folded weight of one norm: Wf [rows,768] = W o w rounded to dtype, c [rows] = row sums of Wf.
 int launch_fold_weight(mbert_dtype dt, const void* W, const void* w, int rows, void* Wf,
                        float* c, hipStream_t s);
@@ -260,9 +263,9 @@ int launch_rope(mbert_dtype dt, void* qkv, int total, const int32_t* meta, const
 // (xs_out, 16-bit types) the residual rounded to dtype, for a folded LayerNorm next.
 int launch_linear_residual(mbert_dtype dt, const void* a, int K, int total, const int32_t* meta,
                            const void* W, float* resid, hipStream_t s, void* xs_out = nullptr,
-                           float2* stats_out = nullptr);
+                           float2* stats_out = nullptr, bool host_rows = false);
 int launch_geglu(mbert_dtype dt, const void* h, int total, const int32_t* meta, const void* Wi,
-                 void* m, hipStream_t s, const FoldArgs* fold = nullptr);
+                 void* m, hipStream_t s, const FoldArgs* fold = nullptr, bool host_rows = false);
 int launch_attention(mbert_dtype dt, const void* qkv, int total, const int32_t* meta, int n_seqs,
                      int is_global, int W, void* o, hipStream_t s);
 }  // namespace mbh

@@ -798,7 +798,7 @@ int launch_mfma_probe(mbert_dtype dt, int blocks, int iters, float* out, hipStre
 
 int launch_qkv(mbert_dtype dt, const void* h, int total, const int32_t* meta, const void* W,
                const float* rope, int max_pos, int table, int apply_rope, void* qkv,
-               hipStream_t s, const FoldArgs* fold) {
+               hipStream_t s, const FoldArgs* fold, bool host_rows) {
     GemmArgs a{};
     if (fold) {
         a.cfold = fold->c;
@@ -808,7 +808,7 @@ int launch_qkv(mbert_dtype dt, const void* h, int total, const int32_t* meta, co
     a.A = h;
     a.B = W;
     a.M = total;
-    a.counts = meta;
+    a.counts = host_rows ? nullptr : meta;
     a.K = D;
     a.N = QKV;
     a.C = qkv;
@@ -825,14 +825,14 @@ int launch_qkv(mbert_dtype dt, const void* h, int total, const int32_t* meta, co
 
 int launch_linear_residual(mbert_dtype dt, const void* a_, int K, int total, const int32_t* meta,
                            const void* W, float* resid, hipStream_t s, void* xs_out,
-                           float2* stats_out) {
+                           float2* stats_out, bool host_rows) {
     GemmArgs a{};
     a.xs_out = xs_out;
     a.stats_out = stats_out;
     a.A = a_;
     a.B = W;
     a.M = total;
-    a.counts = meta;
+    a.counts = host_rows ? nullptr : meta;
     a.K = K;
     a.N = D;
     a.C = resid;
@@ -845,7 +845,7 @@ int launch_linear_residual(mbert_dtype dt, const void* a_, int K, int total, con
 }
 
 int launch_geglu(mbert_dtype dt, const void* h, int total, const int32_t* meta, const void* Wi,
-                 void* m, hipStream_t s, const FoldArgs* fold) {
+                 void* m, hipStream_t s, const FoldArgs* fold, bool host_rows) {
     GemmArgs a{};
     if (fold) {
         a.cfold = fold->c;
@@ -855,7 +855,7 @@ int launch_geglu(mbert_dtype dt, const void* h, int total, const int32_t* meta, 
     a.A = h;
     a.B = Wi;
     a.M = total;
-    a.counts = meta;
+    a.counts = host_rows ? nullptr : meta;
     a.K = D;
     a.N = 2 * FF;
     a.C = m;
