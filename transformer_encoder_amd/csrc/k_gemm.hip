@@ -421,6 +421,8 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 rrstd[tid] = 1.0f / sqrtf(var + p.eps);
             }
             if (tid < BN) cst[tid] = fc;
+        } else if (tid < BM) {
+            rrstd[tid] = 1.0f;  // the epilogue scales by rstd with or without a fold
         }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(GW * (DS - 1)));
@@ -570,7 +572,8 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 rpos[i][k] = min(max(rpos[i][k], 0), p.max_pos - 1);
             }
     }
-    // out = rstd * acc for tile row tr (0 .. BM-1); acc started at -mean * c
+    // out = rstd * acc for tile row tr (0 .. BM-1); acc started at -mean * c. Unconditional
+    // (rstd is 1 without a fold): no branch keeps the rstd reads from being issued early
     auto fold8 = [&](float* v, int tr, int tc) {
         (void)tc;
         const float r = rrstd[tr];
@@ -596,7 +599,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 const int idx = tid + NT * k, sr = idx / CH, c = idx % CH, row = tile_row(sr);
                 float v[8];
                 load8(Cs + sr * CP + 8 * c, v);
-                if (fold) fold8(v, row - m0, 8 * c);
+                fold8(v, row - m0, 8 * c);
                 buf_store8<T>(cbase, cext, (unsigned)((row - m0) * cpitch + (bn * BN + 8 * c) * (int)sizeof(T)), v);
             }
         } else if constexpr (EPI == EPI_ROPE) {
@@ -609,10 +612,8 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 const float* x = Cs + sr * CP + HD * hh + 8 * pc;
                 load8(x, x1);
                 load8(x + 32, x2);
-                if (fold) {
-                    fold8(x1, row - m0, HD * hh + 8 * pc);
-                    fold8(x2, row - m0, HD * hh + 8 * pc + 32);
-                }
+                fold8(x1, row - m0, HD * hh + 8 * pc);
+                fold8(x2, row - m0, HD * hh + 8 * pc + 32);
                 if (rot) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
@@ -686,10 +687,8 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 float g[8], u[8];
                 load8(Cs + sr * CP + 8 * c, g);
                 load8(Cs + sr * CP + HALF + 8 * c, u);
-                if (fold) {
-                    fold8(g, row - m0, 8 * c);
-                    fold8(u, row - m0, HALF + 8 * c);
-                }
+                fold8(g, row - m0, 8 * c);
+                fold8(u, row - m0, HALF + 8 * c);
 #pragma unroll
                 for (int q = 0; q < 8; ++q) g[q] = gelu_erf(g[q]) * u[q];
                 buf_store8<T>(cbase, cext, (unsigned)((row - m0) * cpitch + (bn * HALF + 8 * c) * (int)sizeof(T)), g);
