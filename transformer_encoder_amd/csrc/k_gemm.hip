@@ -298,20 +298,20 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     constexpr int S_CH = BN / 4;
     constexpr int S_IT = EPI == EPI_RESID ? (NWM * 32) * S_CH / (64 * NWM * NWN) : 1;
     static_assert(EPI != EPI_ROPE || (NWM * 32) * R_NHT * 4 % (64 * NWM * NWN) == 0, "items split evenly");
+    // RoPE epilogue items: item k of a thread is head (tid / 4) % R_HPT + R_HPT * k of staged row
+    // tid / (4 R_HPT) at 8-frequency chunk tid % 4, so a thread's items share one {cos, sin} load
+    constexpr int R_HPT = R_NHT / R_IT;
+    static_assert(EPI != EPI_ROPE || R_NHT % R_IT == 0, "items of a thread share a row");
     static_assert(EPI != EPI_RESID || (NWM * 32) * S_CH % (64 * NWM * NWN) == 0, "items split evenly");
     const bool rot = EPI == EPI_ROPE && bn * BN < 2 * D;  // query and key columns are rotated
-    int rpos[(BM / NWM) / 32][R_IT];
-    float4 rcs[2][R_IT][4];
+    int rpos[(BM / NWM) / 32];
+    float4 rcs[2][4];
     f32x4 rold[2][S_IT];
     float4 fbias[EPI == EPI_BIAS_F32 ? (NWM * 32) * S_CH / (64 * NWM * NWN) : 1];
     if constexpr (EPI == EPI_ROPE) {  // raw positions; clamped after the main loop
 #pragma unroll
         for (int i = 0; i < (BM / NWM) / 32; ++i)
-#pragma unroll
-            for (int k = 0; k < R_IT; ++k) {
-                const int sr = (tid0 + 64 * NWM * NWN * k) / (4 * R_NHT);
-                rpos[i][k] = p.pos[min(tile_row_of(i, sr), M - 1)];
-            }
+            rpos[i] = p.pos[min(tile_row_of(i, tid0 / (4 * R_HPT)), M - 1)];
     } else if constexpr (EPI == EPI_BIAS_F32) {
 #pragma unroll
         for (int k = 0; k < (int)(sizeof(fbias) / sizeof(fbias[0])); ++k)
@@ -541,13 +541,9 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     const unsigned xext = (unsigned)min((size_t)(M - m0) * D * sizeof(T), (size_t)0xFFFFFFFFu);
     auto issue_loads = [&](int i) {
         if constexpr (EPI == EPI_ROPE) {  // value tiles load (and ignore) the table too
+            const float4* t = reinterpret_cast<const float4*>(p.rope + (size_t)rpos[i] * (HD / 2) + 8 * (tid & 3));
 #pragma unroll
-            for (int k = 0; k < R_IT; ++k) {
-                const int pc = (tid + NT * k) & 3;
-                const float4* t = reinterpret_cast<const float4*>(p.rope + (size_t)rpos[i][k] * (HD / 2) + 8 * pc);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) rcs[i & 1][k][q] = t[q];
-            }
+            for (int q = 0; q < 4; ++q) rcs[i & 1][q] = t[q];
         } else if constexpr (EPI == EPI_RESID) {
 #pragma unroll
             for (int k = 0; k < S_IT; ++k) {
@@ -565,12 +561,10 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     // the compiler from starting their arithmetic (and so waiting for them) before the loop.
     if constexpr (EPI == EPI_ROPE) {
 #pragma unroll
-        for (int i = 0; i < (BM / NWM) / 32; ++i)
-#pragma unroll
-            for (int k = 0; k < R_IT; ++k) {
-                asm volatile("" : "+v"(rpos[i][k]));
-                rpos[i][k] = min(max(rpos[i][k], 0), p.max_pos - 1);
-            }
+        for (int i = 0; i < (BM / NWM) / 32; ++i) {
+            asm volatile("" : "+v"(rpos[i]));
+            rpos[i] = min(max(rpos[i], 0), p.max_pos - 1);
+        }
     }
     // out = rstd * acc for tile row tr (0 .. BM-1); acc started at -mean * c. Unconditional
     // (rstd is 1 without a fold): no branch keeps the rstd reads from being issued early
@@ -606,8 +600,8 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
             const int c0 = bn * BN;
 #pragma unroll
             for (int k = 0; k < R_IT; ++k) {
-                const int idx = tid + NT * k;
-                const int pc = idx & 3, hh = (idx >> 2) % R_NHT, sr = idx / (4 * R_NHT), row = tile_row(sr);
+                const int pc = tid & 3, hh = (tid >> 2) % R_HPT + R_HPT * k, sr = tid / (4 * R_HPT);
+                const int row = tile_row(sr);
                 float x1[8], x2[8];
                 const float* x = Cs + sr * CP + HD * hh + 8 * pc;
                 load8(x, x1);
@@ -617,7 +611,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
                 if (rot) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const float4 t = rcs[i & 1][k][q];
+                        const float4 t = rcs[i & 1][q];
                         const float a0 = x1[2 * q], b0 = x2[2 * q], a1 = x1[2 * q + 1], b1 = x2[2 * q + 1];
                         x1[2 * q] = a0 * t.x - b0 * t.y;
                         x2[2 * q] = b0 * t.x + a0 * t.y;
