@@ -76,6 +76,12 @@
 #ifndef MB_GEMM_BIG_RB
 #define MB_GEMM_BIG_RB 128
 #endif
+// 32-row block-rows of each wave staged per epilogue pass on the 256x256 tiles (except the
+// residual epilogue, whose prefetched old residual would double): two passes of 128 rows
+// instead of four of 64, half the barriers and twice the independent work between them.
+#ifndef MB_GEMM_EPB
+#define MB_GEMM_EPB 2
+#endif
 #ifndef MB_GEMM_BIG_MIN_TILES
 #define MB_GEMM_BIG_MIN_TILES 512
 #endif
@@ -274,7 +280,10 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     constexpr int KT = ROWB / (int)sizeof(T);
     constexpr int WM = BM / NWM, WN = BN / NWN, FM = WM / 32, FN = WN / 32;
     constexpr int CP = BN + 8;                            // epilogue staging pitch (floats)
-    constexpr int EROWS = NWM * 32;                       // rows staged per epilogue pass
+    constexpr int EPB = (BM == 256 && EPI != EPI_RESID) ? MB_GEMM_EPB : 1;  // block-rows a pass
+    static_assert(FM % EPB == 0, "passes of whole block-rows");
+    constexpr int NPASS = FM / EPB;                       // epilogue passes
+    constexpr int EROWS = NWM * 32 * EPB;                 // rows staged per epilogue pass
     constexpr int MAIN_BYTES = DS * (BM + BN) * ROWB;
     constexpr int EPI_BYTES = EROWS * CP * 4;
     // folded GEMMs: mean and rstd per tile row and c per column, in LDS of their own beyond
@@ -291,26 +300,29 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     if (!xcd_tile(blockIdx.x, (M + BM - 1) / BM, nbn, M, p.N, bm, bn)) return;
     const int m0 = bm * BM;
     const int tid0 = threadIdx.x;
-    // staged epilogue row sr of pass i holds tile row (sr / 32) * WM + 32 * i + sr % 32
-    auto tile_row_of = [&](int i, int sr) { return m0 + (sr >> 5) * (BM / NWM) + 32 * i + (sr & 31); };
+    // staged epilogue row sr of pass i holds row sr % 32 of block-row EPB * i + (sr / 32) % EPB
+    // of wave row sr / (32 EPB)
+    auto tile_row_of = [&](int i, int sr) {
+        return m0 + (sr / (32 * EPB)) * (BM / NWM) + 32 * (EPB * i + (sr >> 5) % EPB) + (sr & 31);
+    };
     constexpr int R_NHT = BN / HD > 0 ? BN / HD : 1;
-    constexpr int R_IT = EPI == EPI_ROPE ? (NWM * 32) * R_NHT * 4 / (64 * NWM * NWN) : 1;
+    constexpr int R_IT = EPI == EPI_ROPE ? EROWS * R_NHT * 4 / (64 * NWM * NWN) : 1;
     constexpr int S_CH = BN / 4;
-    constexpr int S_IT = EPI == EPI_RESID ? (NWM * 32) * S_CH / (64 * NWM * NWN) : 1;
-    static_assert(EPI != EPI_ROPE || (NWM * 32) * R_NHT * 4 % (64 * NWM * NWN) == 0, "items split evenly");
+    constexpr int S_IT = EPI == EPI_RESID ? EROWS * S_CH / (64 * NWM * NWN) : 1;
+    static_assert(EPI != EPI_ROPE || EROWS * R_NHT * 4 % (64 * NWM * NWN) == 0, "items split evenly");
     // RoPE epilogue items: item k of a thread is head (tid / 4) % R_HPT + R_HPT * k of staged row
     // tid / (4 R_HPT) at 8-frequency chunk tid % 4, so a thread's items share one {cos, sin} load
     constexpr int R_HPT = R_NHT / R_IT;
     static_assert(EPI != EPI_ROPE || R_NHT % R_IT == 0, "items of a thread share a row");
-    static_assert(EPI != EPI_RESID || (NWM * 32) * S_CH % (64 * NWM * NWN) == 0, "items split evenly");
+    static_assert(EPI != EPI_RESID || EROWS * S_CH % (64 * NWM * NWN) == 0, "items split evenly");
     const bool rot = EPI == EPI_ROPE && bn * BN < 2 * D;  // query and key columns are rotated
-    int rpos[(BM / NWM) / 32];
+    int rpos[NPASS];
     float4 rcs[2][4];
     f32x4 rold[2][S_IT];
     float4 fbias[EPI == EPI_BIAS_F32 ? (NWM * 32) * S_CH / (64 * NWM * NWN) : 1];
     if constexpr (EPI == EPI_ROPE) {  // raw positions; clamped after the main loop
 #pragma unroll
-        for (int i = 0; i < (BM / NWM) / 32; ++i)
+        for (int i = 0; i < NPASS; ++i)
             rpos[i] = p.pos[min(tile_row_of(i, tid0 / (4 * R_HPT)), M - 1)];
     } else if constexpr (EPI == EPI_BIAS_F32) {
 #pragma unroll
@@ -516,8 +528,8 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
-    // ---- epilogue, in FM passes: pass i stages block-row i of every wave (EROWS tile rows)
-    //      through LDS. A lane holds column (lane & 31) of each 32x32 block and rows
+    // ---- epilogue, in NPASS passes: pass i stages block-rows EPB i .. EPB i + EPB - 1 of every
+    //      wave (EROWS tile rows) through LDS. A lane holds column (lane & 31) of each 32x32 block and rows
     //      8 * (e / 4) + 4 * (lane / 32) + (e % 4) for accumulator element e.
     // The vector-memory counter is shared by loads and stores and retires in order, so a pass
     // that waited for its own loads after the previous pass's stores would also wait for those
@@ -561,7 +573,7 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     // the compiler from starting their arithmetic (and so waiting for them) before the loop.
     if constexpr (EPI == EPI_ROPE) {
 #pragma unroll
-        for (int i = 0; i < (BM / NWM) / 32; ++i) {
+        for (int i = 0; i < NPASS; ++i) {
             asm volatile("" : "+v"(rpos[i]));
             rpos[i] = min(max(rpos[i], 0), p.max_pos - 1);
         }
@@ -576,14 +588,17 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     };
     issue_loads(0);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < NPASS; ++i) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int b = 0; b < EPB; ++b)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                Cs[(wm * 32 + 8 * (e >> 2) + rq + (e & 3)) * CP + wn * WN + 32 * j + lrow] = acc[i][j][e];
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    Cs[(wm * 32 * EPB + 32 * b + 8 * (e >> 2) + rq + (e & 3)) * CP + wn * WN + 32 * j + lrow] =
+                        acc[EPB * i + b][j][e];
         lds_barrier();
-        if (i + 1 < FM) issue_loads(i + 1);
+        if (i + 1 < NPASS) issue_loads(i + 1);
         auto tile_row = [&](int sr) { return tile_row_of(i, sr); };
         if constexpr (EPI == EPI_STORE) {
             constexpr int CH = BN / 8, IT = EROWS * CH / NT;
