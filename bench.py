@@ -237,10 +237,11 @@ def profile_summary(trace_dir: str, wid: int, commands: list):
     ds = 4 if wl.dtype == "f32" else 2
     slots = int(b["mask"].size) if wl.layout == "padded" else T
     best = None
+    # the embedding launch covers 8 rows per workgroup of 256 threads
+    full_grid = ((slots + 7) // 8) * 256
     for f, rows in _trace_rows(trace_dir, "*kernel_trace.csv"):
         emb = [r for r in rows if "embed_ln_kernel" in r["Kernel_Name"]]
-        # the embedding launch covers 8 rows per workgroup of 256 threads
-        if emb and int(emb[0]["Grid_Size_X"]) == ((slots + 7) // 8) * 256:
+        if emb and int(emb[0]["Grid_Size_X"]) == full_grid:
             best = (f, rows)
     if best is None:
         raise SystemExit(f"no trace of workload {wl.name} under {trace_dir}")
@@ -266,14 +267,25 @@ def profile_summary(trace_dir: str, wid: int, commands: list):
         nxt = start[order[j + 1]] if j + 1 < len(order) else None
         alone[i] = start[i] >= run_end and (nxt is None or end[i] <= nxt)
         run_end = max(run_end, end[i])
-    # whole-batch launches only: the largest grid each kind was launched with (the grouped
-    # forward's per-group launches have smaller grids)
+    # whole-batch launches only: a forward's launches count when its embedding launch covered
+    # the whole batch (the batch-size sweep's forwards on fewer sequences do not; a persistent
+    # GEMM's grid is one workgroup per CU whatever the batch, so its grid does not tell), and
+    # of those the largest grid each kind was launched with (the grouped forward's per-group
+    # launches have smaller grids)
     names = [k if k is not None else "other: " + r["Kernel_Name"].split("(")[0][:60]
              for r, k in zip(rows, kinds)]
     grid = [int(r.get("Grid_Size_X", 0) or 0) for r in rows]
+    in_full = [False] * len(rows)
+    for idx in by_stream.values():
+        cur = False
+        for i in idx:
+            if kinds[i] == "embed_ln":
+                cur = grid[i] == full_grid
+            in_full[i] = cur
+    whole = [names[i].startswith("other") or in_full[i] for i in range(len(rows))]
     gmax = {}
     for i, k in enumerate(names):
-        if alone[i]:
+        if alone[i] and whole[i]:
             gmax[k] = max(gmax.get(k, 0), grid[i])
     per, total_ns, n_over, n_part = {}, 0.0, {}, 0
     for i, k in enumerate(names):
@@ -281,7 +293,7 @@ def profile_summary(trace_dir: str, wid: int, commands: list):
         if not alone[i]:
             n_over[k] = n_over.get(k, 0) + 1
             continue
-        if grid[i] != gmax[k]:
+        if not whole[i] or grid[i] != gmax[k]:
             n_part += 1
             continue
         total_ns += d
@@ -291,9 +303,11 @@ def profile_summary(trace_dir: str, wid: int, commands: list):
           "`bench.py --profile-summary`):", "", "```", *commands, "```", "",
           f"Trace file: `{os.path.relpath(f, ROOT)}` (the process of this workload). Launches "
           "that overlapped another kernel in time (the multi-stream legs: "
-          f"{sum(n_over.values())} launches) and launches on part of the batch (a smaller grid "
-          f"than the kind's largest: the grouped forward's per-group launches, {n_part}) are left "
-          "out; every other launch of the process is counted.", "",
+          f"{sum(n_over.values())} launches) and launches on part of the batch (forwards whose "
+          "embedding launch did not cover the whole batch, as the batch-size sweep's, and "
+          "launches with a smaller grid than the kind's largest, as the grouped forward's "
+          f"per-group launches: {n_part}) are left out; every other launch of the process is "
+          "counted.", "",
           "| kernel kind | launches | mean us | total ms | share % | bound | achieved | of peak |",
           "|---|---:|---:|---:|---:|---|---:|---:|"]
     for k, ds_ in sorted(per.items(), key=lambda kv: -sum(kv[1])):

@@ -74,6 +74,10 @@ def test_profile_summary_leaves_out_overlapping_launches(tmp_path, monkeypatch):
         launch(name, 100, grid_x=grid if name == EMBED else 64)
     # a launch on part of the batch (smaller grid, as a grouped forward's): left out
     launch(QKV, 40, grid_x=16)
+    # a forward on fewer sequences (a smaller embedding grid, as the batch-size sweep's) whose
+    # kernels have the whole batch's grids (a persistent GEMM's one workgroup per CU): left out
+    for name in forward_names():
+        launch(name, 50, grid_x=grid // 2 if name == EMBED else 64)
     # a second stream's forward overlapping a first-stream one (QKV 1000 ns, both left out)
     base = t
     for k, name in enumerate(forward_names()):
@@ -89,7 +93,8 @@ def test_profile_summary_leaves_out_overlapping_launches(tmp_path, monkeypatch):
     assert cells[2] == "4" and float(cells[3]) == pytest.approx(0.1)  # 4 launches of 100 ns
     m = re.search(r"\((\d+) launches\)|legs: (\d+) launches", md)
     assert m and int(m.group(2)) == 2 * len(forward_names())
-    assert "per-group launches, 1)" in md
+    # the grid-16 launch and the 22 classified launches of the smaller forward
+    assert "per-group launches: 23)" in md
     # the attention kinds of the serial forward: layers 0 and 3 global, 1 and 2 local
     g = next(ln for ln in md.splitlines() if ln.startswith("| attn_global |"))
     assert [c.strip() for c in g.split("|")][2] == "2"
