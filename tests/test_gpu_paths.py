@@ -172,3 +172,38 @@ def test_mfma_probe_runs_and_is_deterministic(dtype):
     o = host(out).reshape(blocks, 256)
     assert np.all(np.isfinite(o))
     assert np.all(o == o[0:1])
+
+
+def test_padded_batch_far_above_its_tokens_equals_packed():
+    """A padded batch of 16 rows of 2048 slots holding 700-2048 tokens each: the GEMMs get
+    the slot count (32,768) as their row bound and the real count (about 22k) on the device,
+    so the persistent 256x256 tiles walk the slots of the device count, not of the bound. The
+    padded forward's real rows and pooled vectors are bitwise those of the packed forward on
+    the unpadded batch (whose GEMMs take the exact host count), its pad rows exactly zero;
+    one short sequence of the batch is also checked against the oracle."""
+    from transformer_encoder_amd.model import DeviceModel
+    from workloads import pad_batch
+    g = np.random.default_rng([77, 1])
+    lengths = g.integers(700, 2049, size=16)
+    b = random_batch(lengths, 77)
+    dims = Dims(n_layers=2)
+    w = make_weights(dims, "bf16", 77)
+    m = DeviceModel(w, "bf16")
+    ids_pad, mask = pad_batch(b["ids"], b["cu_seqlens"], 2048)
+    out_pad, pooled_pad, _ = m.encode_padded(dev_i32(ids_pad), dev_i32(mask))
+    out, pooled, _ = m.encode(dev_i32(b["ids"]), dev_i32(b["cu_seqlens"]))
+    got_pad = host(out_pad).reshape(-1, 768)
+    u = O.unpad(ids_pad, mask)
+    print(f"T={int(b['cu_seqlens'][-1])} slots={mask.size}", flush=True)
+    assert np.array_equal(got_pad[u["indices"]], host(out))
+    assert np.array_equal(host(pooled_pad), host(pooled))
+    pads = np.ones(got_pad.shape[0], bool)
+    pads[u["indices"]] = False
+    assert np.all(got_pad[pads] == 0.0)
+    # the shortest sequence against the oracle (its rows do not depend on the others)
+    s = int(np.argmin(lengths))
+    cu = b["cu_seqlens"]
+    one = {"ids": b["ids"][cu[s]:cu[s + 1]], "cu_seqlens": np.array([0, lengths[s]])}
+    ref, rpool = O.encode(one["ids"], one["cu_seqlens"], w, O.Config(n_layers=2))
+    check_16bit(host(out)[cu[s]:cu[s + 1]], ref, "shortest sequence tokens")
+    check_16bit(host(pooled)[s:s + 1], rpool, "shortest sequence pooled")
