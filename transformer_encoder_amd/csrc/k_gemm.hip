@@ -34,7 +34,9 @@
 // operand stage lands) and the epilogue scales them by rstd; the residual epilogue can also
 // write the new residual's chunk statistics and its dtype copy for the next such GEMM.
 // Work distribution: tiles are spread over the 8 XCDs in contiguous ranges counted from the
-// real row count read on the device (the padded path sizes its grid for B * Tpad rows).
+// real row count read on the device (the padded path sizes its grid for B * Tpad rows). The
+// 256x256 tiles of the QKV and Wi GEMMs are persistent: one workgroup per CU walks its XCD's
+// tile slots and issues the next tile's loads during the current tile's epilogue.
 #include "common.hpp"
 
 // Operand staging: the number of LDS stages per tile shape (two for the 2304-wide GEMMs, three
