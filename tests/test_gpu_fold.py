@@ -103,3 +103,44 @@ def test_folded_steps_against_oracle(dtype, pattern):
         e = rel_err(host(out), ref)
         print(f"{dtype} {pattern} folded {name}: rel_err={e:.3e}", flush=True)
         assert e <= TOL_STEP[dtype], name
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("T", [14337, 65537])
+def test_folded_persistent_tiles_against_oracle(dtype, T):
+    """The folded QKV + RoPE and Wi + GeGLU GEMMs on the persistent 256x256 tiles: 14,337 rows
+    (57 row tiles, the last holding one row, so some XCDs' slots have no tile) and 65,537 rows
+    (about nine tiles a workgroup, the last again one row). Each against LayerNorm + Linear
+    of the oracle on the same rounded residual, at the per-step bar."""
+    t = torch()
+    dt = B().DTYPES[dtype]
+    lengths = [8192] * (T // 8192) + ([T % 8192] if T % 8192 else [])
+    cu = cu_from_lengths(lengths)
+    meta = meta_for(cu, T)
+    x = _residual(T, "normal", 11)
+    xs = dev(x, dtype)
+    x = host(xs)  # the residual as the GEMM reads it, rounded to the dtype
+    chunks = x.reshape(T, 12, 64)
+    mean = chunks.mean(axis=2)
+    st = np.stack([mean, ((chunks - mean[:, :, None]) ** 2).sum(axis=2)], axis=2)
+    stats = t.from_numpy(st.astype(np.float32)).cuda()
+    cfg = B().mbert_default_config()
+    rope = t.empty(B().mbert_rope_table_floats(cfg), dtype=t.float32, device="cuda")
+    B().mbert_build_rope_tables(cfg, rope)
+    rows = np.r_[0:300, T // 2 - 150:T // 2 + 150, T - 300:T]  # sampled rows, both ends
+    for kind, name in ((B().FOLD_QKV_ROPE, "qkv"), (B().FOLD_GEGLU, "geglu")):
+        W = random_matrix((2304, 768), 91 + kind, dtype=dtype, std=0.02)
+        nw = host(dev((1.0 + 0.02 * np.random.default_rng([92 + kind, 0]).standard_normal(768)), dtype))
+        Wf = t.empty((2304, 768), dtype=_tdt(dtype), device="cuda")
+        c = t.empty(2304, dtype=t.float32, device="cuda")
+        B().mbert_fold_weight(dt, dev(W, dtype), dev(nw, dtype), 2304, Wf, c)
+        out = t.empty((T, 2304 if kind == B().FOLD_QKV_ROPE else 1152), dtype=_tdt(dtype), device="cuda")
+        B().mbert_folded_gemm(dt, kind, xs, stats, T, meta, Wf, c, 1e-5, rope, 8192, 1, out)
+        h = O.layernorm(x[rows], nw, 1e-5)
+        if kind == B().FOLD_QKV_ROPE:
+            ref = O.qkv_projection(h, W, O.positions(cu)[rows], 10000.0, O.Config())
+        else:
+            ref = O.mlp_in_geglu(h, W, O.Config())
+        e = rel_err(host(out)[rows], ref)
+        print(f"{dtype} T={T} folded {name}: rel_err={e:.3e}", flush=True)
+        assert e <= TOL_STEP[dtype], name
