@@ -78,9 +78,9 @@
 #ifndef MB_GEMM_BIG_RB
 #define MB_GEMM_BIG_RB 128
 #endif
-// 32-row block-rows of each wave staged per epilogue pass on the 256x256 tiles (except the
-// residual epilogue, whose prefetched old residual would double): two passes of 128 rows
-// instead of four of 64, half the barriers and twice the independent work between them.
+// 32-row block-rows of each wave staged per epilogue pass on non-persistent 256x256 QKV and
+// Wi tiles (the persistent layout has no LDS for it): two passes of 128 rows instead of four
+// of 64, half the barriers and twice the independent work between them.
 #ifndef MB_GEMM_EPB
 #define MB_GEMM_EPB 2
 #endif
@@ -215,9 +215,13 @@ __device__ __forceinline__ bool xcd_tile(int hw_id, int nbm, int nbn, int M, int
 
 // Workgroups of a persistent GEMM launch: one per CU of the MI355X (256 CUs in 8 XCDs).
 constexpr int GEMM_PERSIST_WG = 256;
-// Persistent on the 256x256 tiles, except the residual epilogue (its prefetched old residual
-// leaves no registers for the next tile's loads).
-constexpr bool gemm_persistent(int bm, int epi) { return MB_GEMM_PERSIST && bm == 256 && epi != EPI_RESID; }
+// Persistent on the 256x256 tiles of the forward's QKV and Wi GEMMs (RoPE and GeGLU
+// epilogues); not the residual epilogue (its prefetched old residual leaves no registers for
+// the next tile's loads; a persistent build spilled), the plain store (spilled too) nor the
+// heads' fp32 epilogues.
+constexpr bool gemm_persistent(int bm, int epi) {
+    return MB_GEMM_PERSIST && bm == 256 && (epi == EPI_ROPE || epi == EPI_GEGLU);
+}
 
 // Grid size covering every split the device may choose for any row count up to M.
 inline int xcd_gemm_grid(int M, int BM, int N, int BN) {
@@ -298,7 +302,8 @@ __global__ __launch_bounds__(64 * NWM * NWN, OCC) void gemm_kernel(GemmArgs p) {
     constexpr int CP = BN + 8;                            // epilogue staging pitch (floats)
     constexpr bool PERSIST = gemm_persistent(BM, EPI);
     static_assert(!PERSIST || DS == 2, "persistent tiles prefetch into the first of two stages");
-    constexpr int EPB = (!PERSIST && BM == 256 && EPI != EPI_RESID) ? MB_GEMM_EPB : 1;  // block-rows a pass
+    constexpr int EPB = (!PERSIST && BM == 256 && (EPI == EPI_ROPE || EPI == EPI_STORE || EPI == EPI_GEGLU))
+                            ? MB_GEMM_EPB : 1;  // block-rows a pass
     static_assert(FM % EPB == 0, "passes of whole block-rows");
     constexpr int NPASS = FM / EPB;                       // epilogue passes
     constexpr int EROWS = NWM * 32 * EPB;                 // rows staged per epilogue pass
