@@ -228,9 +228,9 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(
     // masking and max exchange below). A step holds 16 KS groups of 1 KB (per key tile 8 of
     // K, then 8 of V; group j = rows 8j .. 8j+7); wave w fills groups w, w + NWV, ...: lane L
     // row 8j + L / 8 at physical chunk L % 8, which holds the logical chunk that kchunk /
-    // vchunk place there (both swizzles are their own inverses). Rows past the last key
-    // re-read it, like the register path. One buffer descriptor per key tile, based at its
-    // first key, so offsets stay small for any sequence length.
+    // vchunk place there (both swizzles are their own inverses). One buffer descriptor per
+    // key tile, based at its first key and ending at the sequence's last, so offsets stay small
+    // for any sequence length and rows past the end load zeros.
     constexpr int NWV = 4 * KS, GPW = 16 * KS / NWV;
     static_assert(F32 || sizeof(Ks[0]) == sizeof(Vs[0]), "K and V stages of one size");
     constexpr unsigned SSTR = (unsigned)sizeof(Ks[0]);  // bytes between stages
@@ -249,14 +249,21 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(
         dst0[i] = (isv ? reinterpret_cast<unsigned char*>(&Vs[0][hh][0])
                        : reinterpret_cast<unsigned char*>(&Ks[0][hh][0])) + 1024 * j;
     }
+    // per-lane offsets within a key tile are loop constants; the tile's first key goes into the
+    // descriptor base and its row count into the extent, so rows past the sequence's last key
+    // (and a tile past the last) read as zeros, which the masking and the zero probabilities
+    // of those keys leave without effect
+    unsigned voffc[GPW];
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) voffc[i] = (unsigned)drow[i] * (unsigned)(QKV * sizeof(T)) + dcol[i];
     auto dma = [&](int step, int st) {
 #pragma unroll
         for (int i = 0; i < GPW; ++i) {
             const int hh = (NWV * i) / 16;
-            const int kbs = klo + 64 * min(KS * step + hh, nkt - 1);
-            const unsigned voff =
-                (unsigned)min(drow[i], khi - kbs) * (unsigned)(QKV * sizeof(T)) + dcol[i];
-            lds_dma16_buf(qkv + (size_t)kbs * QKV, 64u * QKV * (unsigned)sizeof(T), voff, 0u,
+            const int tix = KS * step + hh;
+            const int kbs = klo + 64 * min(tix, nkt - 1);
+            const int nrows = tix < nkt ? min(64, khi - kbs + 1) : 0;
+            lds_dma16_buf(qkv + (size_t)kbs * QKV, (unsigned)nrows * (unsigned)(QKV * sizeof(T)), voffc[i], 0u,
                           dst0[i] + st * SSTR);
         }
     };
@@ -288,6 +295,15 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(
         sstore(0, 0);
         __syncthreads();
     } else {
+        // the LDS slots this wave's DMA lanes fill start as zeros, so that rows past a sequence's
+        // end hold zeros or earlier keys whether or not the hardware writes its zeros for them
+        // (a masked key's probability is 0, and 0 times a stale non-finite value is not)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < GPW; ++i) *(u32x4*)(dst0[i] + st * SSTR + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+        asm volatile("" ::: "memory");
         dma(0, 0);
         publish();
     }
