@@ -285,9 +285,10 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_kernel(
     }
     float m_run = -INFINITY, l_run = 0.f;
 
-    // Every load is unconditional (a tile past the last re-reads the last one): loads under a
-    // branch leave the wait-count pass unsure of what is in flight. Step i's tiles are held in
-    // register slot i % AP; the loop is unrolled AP times so the slots are static.
+    // Every load is unconditional (a tile past the last re-reads the last one on the fp32 path
+    // and loads zeros on the DMA path): loads under a branch leave the wait-count pass unsure
+    // of what is in flight. Step i's tiles are held in register slot i % AP; the loop is
+    // unrolled AP times so the slots are static.
     const int nst = (nkt + KS - 1) / KS;  // steps of KS key tiles
     if constexpr (F32) {
 #pragma unroll
